@@ -1,0 +1,484 @@
+/*
+ * sage_oracle.c -- plain, slow CPU oracle of SageAttention2-style quantized
+ * non-causal attention (quantize, then attend).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this file.  It shares no code,
+ * header, table or constant with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Sources (page title + section):
+ *   [DESIGN]  "Sage2 Blackwell Mainloop", sections "Decision" and
+ *             "Existing Contract": K mean/smoothing, per-warp (32-row groups
+ *             inside 128-row blocks) INT8 Q, per-block (64-row) INT8 K with the
+ *             mean subtracted, FP8 V with per-channel scales, BF16 NHD output.
+ *   [FLOW]    "State-Ownership Architecture Decision", section
+ *             "Non-Negotiable Dataflow": exact global K mean and V-scale
+ *             prepasses; K64/V64 tiles in strictly increasing order; per tile
+ *             QK, score scaling, max update, denominator update, FP8
+ *             probability conversion, PV, FP32 RO addition; final exact FP32
+ *             reciprocal of d, then normalisation, V scale and BF16.
+ *   [PAIR]    "Sage2 SM89 Temporal Pair Experiment", section "Candidate": the
+ *             per-tile order QK -> update_mdo -> accumulate_d -> RS_32_to_8 -> PV.
+ *
+ * Arithmetic: every floating-point step below is an IEEE binary32 operation
+ * (round to nearest even), written one operation per statement.  The file is
+ * compiled with -ffp-contract=off, so no multiply-add is ever fused.  Integer
+ * dot products are exact.  Where the pages leave a step open, the reading
+ * taken is stated next to the code.
+ *
+ * Layouts used here are logical and plain:
+ *   Q/K/V inputs: BF16 bit patterns, element (b,n,h,d) at
+ *                 b*stride_b + n*stride_n + h*stride_h + d.
+ *   q_i8  [B][H][Nq][128], Nq = 128*ceil(N/128), rows >= N are 0
+ *   q_scale [B][H][Nq/32]
+ *   k_i8  [B][H][Nk][128], Nk = 64*ceil(N/64), rows >= N are 0
+ *   k_scale [B][H][Nk/64]
+ *   k_mean [B][H][128]
+ *   v8    [B][H][Nk][128] E4M3 bytes, rows >= N are 0x00
+ *   v_scale [B][H][128]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define HD 128      /* head dimension fixed by the contract */
+#define QG 32       /* Q quantization group: 32 rows */
+#define BQ 128      /* Q block: 128 rows (4 groups) */
+#define BK 64       /* K/V tile: 64 rows */
+
+/* Groups whose absolute maximum is below this are encoded as all-zero with a
+ * zero scale.  Reading: the pages do not define the degenerate case; below
+ * 2^-100 the reciprocal scale 127/a or 448/a would approach FP32 overflow. */
+#define AMAX_FLOOR 0x1p-100f
+
+/* ---------------------------------------------------------------- codecs -- */
+
+/* BF16 bits -> FP32 value (exact: BF16 is the top half of a binary32). */
+float oracle_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* FP32 -> BF16 bits, round to nearest, ties to even. NaN stays a quiet NaN. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;             /* carries into the exponent as RNE requires */
+    return (uint16_t)(u >> 16);
+}
+
+/* OCP FP8 E4M3FN byte -> exact value: bias 7, 3 mantissa bits, no infinities,
+ * 0x7F/0xFF are NaN, largest finite magnitude 448, smallest subnormal 2^-9. */
+float oracle_e4m3_decode(uint8_t b)
+{
+    int sign = b >> 7;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    float v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexpf((float)m, -9);            /* m/8 * 2^(1-7) */
+    else
+        v = ldexpf((float)(8 + m), e - 10);  /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Exact values of the 127 non-negative finite E4M3FN codes 0x00..0x7E,
+ * strictly increasing; filled once when the library is loaded. */
+static float e4m3_pos[127];
+
+__attribute__((constructor)) static void e4m3_table_init(void)
+{
+    for (int c = 0; c < 127; ++c)
+        e4m3_pos[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
+/* FP32 -> E4M3FN byte, round to nearest with ties to the even code, finite
+ * values beyond the largest finite magnitude saturate to +-448, sign of zero
+ * kept, NaN -> 0x7F.  Implemented by exact comparison with the two nearest
+ * representable magnitudes (every E4M3 value and every midpoint between two
+ * adjacent ones is exactly representable in binary32). */
+uint8_t oracle_e4m3_encode(float x)
+{
+    if (isnan(x))
+        return 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    float a = fabsf(x);
+    if (a >= 448.0f)
+        return sign | 0x7e;
+    /* binary search: largest code lo in [0,125] with e4m3_pos[lo] <= a */
+    int lo = 0, hi = 126;                  /* invariant: pos[lo] <= a < pos[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_pos[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    float midpoint = (e4m3_pos[lo] + e4m3_pos[hi]) * 0.5f;   /* exact */
+    int code;
+    if (a < midpoint)
+        code = lo;
+    else if (a > midpoint)
+        code = hi;
+    else
+        code = (lo % 2 == 0) ? lo : hi;
+    return sign | (uint8_t)code;
+}
+
+/* ------------------------------------------------------------ utilities -- */
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static float in_val(const uint16_t* base, int64_t sb, int64_t sn, int64_t sh,
+                    int b, int n, int h, int d)
+{
+    return oracle_bf16_to_f32(base[(int64_t)b * sb + (int64_t)n * sn + (int64_t)h * sh + d]);
+}
+
+/* INT8 code of x for reciprocal scale inv: nearest integer (ties to even) of
+ * the FP32 product, clamped to the symmetric range [-127, 127]. */
+static int8_t int8_code(float x, float inv)
+{
+    float y = x * inv;
+    float r = rintf(y);                    /* default rounding mode: ties to even */
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* ---------------------------------------------------------------- steps -- */
+
+/* Step 1: exact global K channel mean.  [DESIGN, Decision: "K mean/smoothing"];
+ * [FLOW: "Keep the exact global K mean"].
+ * Reading: FP32, summed in a fixed two-level order -- within each 64-row tile
+ * in increasing row order starting from +0, then the tile partials in
+ * increasing tile order starting from +0 -- and divided by N (valid rows only)
+ * with one IEEE division. */
+void oracle_k_mean(const uint16_t* K, int64_t sb, int64_t sn, int64_t sh,
+                   int B, int N, int H, float* km)
+{
+    int64_t T = ceil_div(N, BK);
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            float total[HD], part[HD];
+            for (int d = 0; d < HD; ++d) total[d] = 0.0f;
+            for (int64_t j = 0; j < T; ++j) {
+                int64_t n_end = (j + 1) * BK < N ? (j + 1) * BK : N;
+                for (int d = 0; d < HD; ++d) part[d] = 0.0f;
+                for (int64_t n = j * BK; n < n_end; ++n)
+                    for (int d = 0; d < HD; ++d)
+                        part[d] = part[d] + in_val(K, sb, sn, sh, b, (int)n, h, d);
+                for (int d = 0; d < HD; ++d) total[d] = total[d] + part[d];
+            }
+            for (int d = 0; d < HD; ++d)
+                km[((int64_t)b * H + h) * HD + d] = total[d] / (float)N;
+        }
+}
+
+/* Step 2: K smoothing and per-64-row-block INT8 quantization.
+ * [DESIGN, Decision: "K subtract-mean quantization"; Existing Contract:
+ * "Per-block INT8 K with 64-row blocks"]; [FLOW: per-64-row K bytes/scales].
+ * For tile j over rows [64j, min(64j+64, N)):
+ *   kc = fl32(k - km[d]);  a = max |kc| over the valid rows and all channels;
+ *   k_scale = fl32(a / 127);  inv = fl32(127 / a);
+ *   code = clamp(rne(fl32(kc * inv)), -127, 127).
+ * Readings: padded rows (>= N) are excluded from a and hold code 0; symmetric
+ * range +-127; ties to even; multiplication by the reciprocal; a tile with
+ * a < 2^-100 (in particular a == 0) gets scale 0 and all-zero codes. */
+void oracle_quant_k(const uint16_t* K, int64_t sb, int64_t sn, int64_t sh,
+                    int B, int N, int H, const float* km,
+                    int8_t* k_i8, float* k_scale)
+{
+    int64_t T = ceil_div(N, BK);
+    int64_t Nk = T * BK;
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t j = 0; j < T; ++j) {
+                const float* mean = km + ((int64_t)b * H + h) * HD;
+                int8_t* out = k_i8 + (((int64_t)b * H + h) * Nk + j * BK) * HD;
+                int64_t n_end = (j + 1) * BK < N ? (j + 1) * BK : N;
+                float a = 0.0f;
+                for (int64_t n = j * BK; n < n_end; ++n)
+                    for (int d = 0; d < HD; ++d) {
+                        float kc = in_val(K, sb, sn, sh, b, (int)n, h, d) - mean[d];
+                        float m = fabsf(kc);
+                        if (m > a) a = m;
+                    }
+                memset(out, 0, (size_t)BK * HD);
+                float* sc = k_scale + ((int64_t)b * H + h) * T + j;
+                if (!(a >= AMAX_FLOOR)) {
+                    *sc = 0.0f;
+                    continue;
+                }
+                *sc = a / 127.0f;
+                float inv = 127.0f / a;
+                for (int64_t n = j * BK; n < n_end; ++n)
+                    for (int d = 0; d < HD; ++d) {
+                        float kc = in_val(K, sb, sn, sh, b, (int)n, h, d) - mean[d];
+                        out[(n - j * BK) * HD + d] = int8_code(kc, inv);
+                    }
+            }
+}
+
+/* Step 3: per-32-row INT8 Q quantization.  [DESIGN, Existing Contract:
+ * "Per-warp INT8 Q with 128-row blocks and 32-row warp groups"]; [FLOW:
+ * per-32-row Q bytes/scales].  Group g covers rows [32g, min(32g+32, N));
+ * a = max |q|; q_scale = fl32(a/127); inv = fl32(127/a); code as for K.
+ * Readings: the softmax scale is not folded into Q (it enters at score
+ * scaling); groups at or beyond N, and groups with a < 2^-100, have scale 0
+ * and zero codes; padded rows hold 0. */
+void oracle_quant_q(const uint16_t* Q, int64_t sb, int64_t sn, int64_t sh,
+                    int B, int N, int H, int8_t* q_i8, float* q_scale)
+{
+    int64_t Nq = ceil_div(N, BQ) * BQ;
+    int64_t G = Nq / QG;
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t g = 0; g < G; ++g) {
+                int8_t* out = q_i8 + (((int64_t)b * H + h) * Nq + g * QG) * HD;
+                float* sc = q_scale + ((int64_t)b * H + h) * G + g;
+                int64_t r_end = (g + 1) * QG < N ? (g + 1) * QG : N;
+                float a = 0.0f;
+                for (int64_t r = g * QG; r < r_end; ++r)
+                    for (int d = 0; d < HD; ++d) {
+                        float m = fabsf(in_val(Q, sb, sn, sh, b, (int)r, h, d));
+                        if (m > a) a = m;
+                    }
+                memset(out, 0, (size_t)QG * HD);
+                if (!(a >= AMAX_FLOOR)) {
+                    *sc = 0.0f;
+                    continue;
+                }
+                *sc = a / 127.0f;
+                float inv = 127.0f / a;
+                for (int64_t r = g * QG; r < r_end; ++r)
+                    for (int d = 0; d < HD; ++d)
+                        out[(r - g * QG) * HD + d] = int8_code(in_val(Q, sb, sn, sh, b, (int)r, h, d), inv);
+            }
+}
+
+/* Step 4: per-channel V scale and FP8 E4M3 quantization.  [DESIGN, Decision:
+ * "V scale/FP8 quantization"; Existing Contract: "FP8 V and the existing
+ * per-channel scale layout"]; [FLOW: "V scale prepasses"].
+ * For channel (b,h,d): a = max over rows n < N of |v|; v_scale = fl32(a/448);
+ * inv = fl32(448/a); v8 = e4m3(fl32(v * inv)).
+ * Readings: 448 is the largest finite E4M3FN magnitude; rounding to nearest
+ * even with saturation; channels with a < 2^-100 get scale 0 and bytes 0x00;
+ * padded rows hold 0x00. */
+void oracle_quant_v(const uint16_t* V, int64_t sb, int64_t sn, int64_t sh,
+                    int B, int N, int H, uint8_t* v8, float* v_scale)
+{
+    int64_t Nk = ceil_div(N, BK) * BK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            uint8_t* out = v8 + ((int64_t)b * H + h) * Nk * HD;
+            float* sc = v_scale + ((int64_t)b * H + h) * HD;
+            float a[HD], inv[HD];
+            for (int d = 0; d < HD; ++d) a[d] = 0.0f;
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < HD; ++d) {
+                    float m = fabsf(in_val(V, sb, sn, sh, b, n, h, d));
+                    if (m > a[d]) a[d] = m;
+                }
+            for (int d = 0; d < HD; ++d) {
+                if (a[d] >= AMAX_FLOOR) {
+                    sc[d] = a[d] / 448.0f;
+                    inv[d] = 448.0f / a[d];
+                } else {
+                    sc[d] = 0.0f;
+                    inv[d] = 0.0f;
+                }
+            }
+            memset(out, 0, (size_t)Nk * HD);
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < HD; ++d) {
+                    if (sc[d] == 0.0f)
+                        continue;                       /* zero channel: bytes stay 0x00 */
+                    float y = in_val(V, sb, sn, sh, b, n, h, d) * inv[d];
+                    out[(int64_t)n * HD + d] = oracle_e4m3_encode(y);
+                }
+        }
+}
+
+/* Step 5 (score part only): exact int32 QK^T sums for query rows [r0, r1) of
+ * every (b,h) against all Nk (padded) keys.  [FLOW: per-tile "QK"];
+ * [PAIR: "QK"].  s_out is [B][H][r1-r0][Nk]. */
+void oracle_qk_s32(const int8_t* q_i8, const int8_t* k_i8, int B, int N, int H,
+                   int64_t r0, int64_t r1, int32_t* s_out)
+{
+    int64_t Nq = ceil_div(N, BQ) * BQ;
+    int64_t Nk = ceil_div(N, BK) * BK;
+    int64_t R = r1 - r0;
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t r = r0; r < r1; ++r) {
+                const int8_t* q = q_i8 + (((int64_t)b * H + h) * Nq + r) * HD;
+                for (int64_t n = 0; n < Nk; ++n) {
+                    const int8_t* k = k_i8 + (((int64_t)b * H + h) * Nk + n) * HD;
+                    int32_t s = 0;
+                    for (int d = 0; d < HD; ++d)
+                        s += (int32_t)q[d] * (int32_t)k[d];
+                    s_out[(((int64_t)b * H + h) * R + (r - r0)) * Nk + n] = s;
+                }
+            }
+}
+
+/* Steps 5-9 for a list of query rows: the per-tile online-softmax loop and the
+ * epilogue.  [FLOW, Non-Negotiable Dataflow and the tile-t handoff record];
+ * [PAIR, Candidate: QK -> update_mdo -> accumulate_d -> RS_32_to_8 -> PV].
+ *
+ * For row r (group g = r/32) of head (b,h):
+ *   c   = fl32(sm_scale * fl32(log2 e))
+ *   m = -inf, d = +0, RO[0..127] = +0
+ *   for tile j = 0 .. T-1 (strictly increasing, none skipped):
+ *     (a) S_c = exact int32 sum_d q[r,d] k[64j+c,d]            (QK)
+ *     (b) s_j = fl32(fl32(q_scale[g] * k_scale[j]) * c);
+ *         t_c = fl32(fl32(S_c) * s_j)                            (score scaling)
+ *     (c) keys 64j+c >= N: t_c = -inf                            (tail predicate)
+ *     (d) m_new = max(m, max_c t_c)                              (max update)
+ *     (e) alpha = exp2(fl32(m - m_new)); RO = fl32(RO*alpha);
+ *         d = fl32(d*alpha)                                      (old_scale before PV)
+ *     (f) p_c = fl32(448 * exp2(fl32(t_c - m_new))), masked -> 0
+ *     (g) d = fl32(d + p_c) for c = 0..63 in order               (accumulate_d)
+ *     (h) p8_c = e4m3(p_c)                                       (RS_32_to_8)
+ *     (i) pv[e] = fl32(exact sum_c dec(p8_c) * dec(v8[64j+c, e]));
+ *         RO[e] = fl32(RO[e] + pv[e])                            (PV, FP32 RO add)
+ *     m = m_new
+ *   rcp = fl32(1/d); o[e] = bf16(fl32(fl32(RO[e] * rcp) * v_scale[e]))
+ *
+ * Readings: (1) the per-tile PV is exact and rounded once to FP32 before the
+ * ordered RO addition (the pages' FP16 per-tile buffer belongs to an NVIDIA
+ * instruction; the contract kept here is ordered accumulation into FP32 rows).
+ * (2) P is carried scaled by 448 so that probabilities in [0,1] use the normal
+ * range of E4M3; d accumulates the same scaled values, so no constant remains
+ * in the final formula.  (3) d sums the FP32 P before the FP8 conversion
+ * (accumulate_d precedes RS_32_to_8).  (4) The base-2 exponential with log2 e
+ * folded into the score scale; exp2f is the host C library's.
+ * The inner PV sum is exact in binary64: every E4M3 value is an integer times
+ * 2^-9 of magnitude <= 448, so 64 products are integers times 2^-18 whose sum
+ * stays below 2^42.
+ *
+ * rows: array of nrows triples (b, h, r) with r < N.
+ * out_bits: [nrows][128] BF16 bits.  out_f32 (may be NULL): the FP32 value
+ * before BF16 rounding. */
+void oracle_attn_rows(const int8_t* q_i8, const float* q_scale,
+                      const int8_t* k_i8, const float* k_scale,
+                      const uint8_t* v8, const float* v_scale,
+                      int B, int N, int H, float sm_scale,
+                      const int64_t* rows, int64_t nrows,
+                      uint16_t* out_bits, float* out_f32)
+{
+    (void)B;
+    int64_t Nq = ceil_div(N, BQ) * BQ;
+    int64_t T = ceil_div(N, BK);
+    int64_t Nk = T * BK;
+    int64_t G = Nq / QG;
+    const float log2e = 1.4426950408889634f;
+    const float c = sm_scale * log2e;
+    float vdec[256];
+    for (int i = 0; i < 256; ++i)
+        vdec[i] = oracle_e4m3_decode((uint8_t)i);   /* exact value of each byte */
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t b = rows[3 * i + 0], h = rows[3 * i + 1], r = rows[3 * i + 2];
+        int64_t bh = b * H + h;
+        const int8_t* q = q_i8 + (bh * Nq + r) * HD;
+        float qs = q_scale[bh * G + r / QG];
+        float m = -INFINITY, dsum = 0.0f;
+        float RO[HD];
+        for (int e = 0; e < HD; ++e) RO[e] = 0.0f;
+        float t[BK], p[BK];
+        uint8_t p8[BK];
+        for (int64_t j = 0; j < T; ++j) {
+            float sj = (qs * k_scale[bh * T + j]) * c;
+            float tmax = -INFINITY;
+            for (int cc = 0; cc < BK; ++cc) {
+                int64_t n = j * BK + cc;
+                if (n < N) {
+                    const int8_t* k = k_i8 + (bh * Nk + n) * HD;
+                    int32_t s = 0;
+                    for (int d = 0; d < HD; ++d)
+                        s += (int32_t)q[d] * (int32_t)k[d];
+                    t[cc] = (float)s * sj;
+                } else {
+                    t[cc] = -INFINITY;
+                }
+                if (t[cc] > tmax) tmax = t[cc];
+            }
+            float m_new = m > tmax ? m : tmax;
+            float alpha = exp2f(m - m_new);
+            for (int e = 0; e < HD; ++e) RO[e] = RO[e] * alpha;
+            dsum = dsum * alpha;
+            for (int cc = 0; cc < BK; ++cc) {
+                if (j * BK + cc < N) {
+                    float x = t[cc] - m_new;
+                    p[cc] = 448.0f * exp2f(x);
+                } else {
+                    p[cc] = 0.0f;
+                }
+            }
+            for (int cc = 0; cc < BK; ++cc)
+                dsum = dsum + p[cc];
+            for (int cc = 0; cc < BK; ++cc)
+                p8[cc] = oracle_e4m3_encode(p[cc]);
+            for (int e = 0; e < HD; ++e) {
+                double acc = 0.0;
+                for (int cc = 0; cc < BK; ++cc) {
+                    int64_t n = j * BK + cc;
+                    acc += (double)vdec[p8[cc]] * (double)vdec[v8[(bh * Nk + n) * HD + e]];
+                }
+                RO[e] = RO[e] + (float)acc;
+            }
+            m = m_new;
+        }
+        float rcp = 1.0f / dsum;
+        const float* vs = v_scale + bh * HD;
+        for (int e = 0; e < HD; ++e) {
+            float o = (RO[e] * rcp) * vs[e];
+            out_bits[i * HD + e] = oracle_f32_to_bf16(o);
+            if (out_f32) out_f32[i * HD + e] = o;
+        }
+    }
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Array forms of the codecs (plain loops over the scalar functions above). */
+void oracle_e4m3_encode_n(const float* x, uint8_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = oracle_e4m3_encode(x[i]);
+}
+
+void oracle_f32_to_bf16_n(const float* x, uint16_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = oracle_f32_to_bf16(x[i]);
+}
