@@ -1,0 +1,191 @@
+/*
+ * sage_mi355x.h -- C ABI of SageAttention2-style quantized non-causal
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: page titles and sections):
+ *   "Sage2 Blackwell Mainloop", sections "Decision" and "Existing Contract":
+ *     an exact K channel-mean (smoothing) prepass; INT8 Q with one scale per
+ *     32-row group inside 128-row blocks; INT8 K, mean subtracted, with one
+ *     scale per 64-row block; FP8 V with per-channel scales; a fused mainloop
+ *     that takes the INT8 Q/K, FP8 V and the Q/K/V scales and emits the final
+ *     BF16 attention output, contiguous token-major NHD; batch, 56 heads,
+ *     head dimension 128, non-causal, projection-strided BF16 NHD inputs.
+ *   "State-Ownership Architecture Decision", sections "Non-Negotiable
+ *     Dataflow" and "Interface And Future Ulysses Layout": all K64/V64 tiles
+ *     in strictly increasing order; per tile QK, score scaling, max update,
+ *     denominator update, FP8 probability conversion and PV added into FP32
+ *     output rows; never an N-by-N score tensor; never a split of the KV walk;
+ *     the FP32 reciprocal of d then normalisation, V scale and BF16; strided
+ *     NHD inputs consumed directly (no transpose or contiguous copy), output
+ *     rows at [token, head*128 + d].
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers (HIP device memory of the current
+ *     device); shapes, strides and descriptors are host values.
+ *   - The caller owns every buffer.  The library allocates no memory and keeps
+ *     no state except a thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  A kernel fault surfaces at
+ *     the caller's next synchronisation of that stream.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     error nothing is launched and a status other than SAGE_OK is returned,
+ *     with detail in sage_last_error_message().  No exception crosses the ABI.
+ *   - Inputs must be finite BF16 values; non-finite inputs give unspecified
+ *     (but memory-safe) results.
+ */
+#ifndef SAGE_MI355X_H
+#define SAGE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_ABI_VERSION 1
+#define SAGE_HEAD_DIM 128
+
+typedef enum sage_status {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad shape, bad scale     */
+    SAGE_ERR_UNSUPPORTED = 2,       /* legal but unsupported stride/alignment */
+    SAGE_ERR_WORKSPACE = 3,         /* workspace null, misaligned or too small */
+    SAGE_ERR_HIP = 4                /* a HIP launch failed                    */
+} sage_status;
+
+/* Problem shape.  D must be 128; 1 <= B, H; 1 <= N <= 2^24. */
+typedef struct sage_shape {
+    int32_t B, N, H, D;
+} sage_shape;
+
+/* A BF16 [B, N, H, 128] input view with unit stride along D.  Element
+ * (b, n, h, d) is at data + b*stride_b + n*stride_n + h*stride_h + d
+ * (strides in elements).  Supported: strides >= 0 and multiples of 8, data
+ * 16-byte aligned.  Q, K and V may be column slices of one projection buffer
+ * [B, N, 3*H*128] (stride_n = 3*H*128). */
+typedef struct sage_bf16_in {
+    const void* data;
+    int64_t stride_b, stride_n, stride_h;
+} sage_bf16_in;
+
+/* A BF16 [B, N, H, 128] output view, same addressing.  Supported: strides
+ * >= 0 and multiples of 4, data 8-byte aligned.  Only rows n < N are
+ * written. */
+typedef struct sage_bf16_out {
+    void* data;
+    int64_t stride_b, stride_n, stride_h;
+} sage_bf16_out;
+
+/* Quantized operands, carved from one caller-owned workspace by
+ * sage_quantized_carve().  With T = ceil(N/64), Nq = 128*ceil(N/128),
+ * G = Nq/32 and bh = b*H + h, the layouts are:
+ *
+ *   q_i8    INT8 codes, 4096 bytes per (bh, group g):
+ *           byte ((bh*G + g)*4096 + (kk*64 + l)*16 + i)
+ *             = code of Q[b, 32g + l%32, h, 32kk + 16*(l/32) + i]
+ *           for kk in 0..3, l in 0..63, i in 0..15.  Rows >= N hold 0.
+ *   q_scale FP32 [B][H][G]; groups with no row < N hold 0.
+ *   k_i8    INT8 codes of K - k_mean, 8192 bytes per (bh, tile t):
+ *           byte ((bh*T + t)*8192 + ((half*4 + kk)*64 + l)*16 + i)
+ *             = code of K[b, 64t + 32*half + l%32, h, 32kk + 16*(l/32) + i]
+ *           for half in 0..1.  Rows >= N hold 0.
+ *   k_scale FP32 [B][H][T]
+ *   k_mean  FP32 [B][H][128]
+ *   v_fp8   E4M3FN bytes, 8192 bytes per (bh, tile t):
+ *           byte ((bh*T + t)*8192 + ((db*2 + half)*64 + l)*16 + i)
+ *             = code of V[b, 64t + 32*half + 8*(i/4) + 4*(l/32) + i%4, h,
+ *                         32db + l%32]
+ *           for db in 0..3.  Rows >= N hold 0x00.
+ *   v_scale FP32 [B][H][128]
+ *   k_tile_sum, v_tile_amax  FP32 [B][H][T][128], v_inv FP32 [B][H][128]:
+ *           scratch of the prepass (per-tile K channel sums, per-tile V
+ *           channel absolute maxima, per-channel 448/amax).
+ *
+ * The INT8 and E4M3 layouts are the operand layouts of the gfx950 matrix
+ * instructions the mainloop issues, so every mainloop load is a contiguous
+ * 1 KiB row of 16-byte lanes. */
+typedef struct sage_quantized {
+    sage_shape shape;
+    int8_t* q_i8;
+    float* q_scale;
+    int8_t* k_i8;
+    float* k_scale;
+    float* k_mean;
+    uint8_t* v_fp8;
+    float* v_scale;
+    float* k_tile_sum;
+    float* v_tile_amax;
+    float* v_inv;
+} sage_quantized;
+
+/* Bytes of workspace sage_quantized_carve() and sage_attn_fwd() need for
+ * shape s (a pure host function); 0 if s is invalid. */
+size_t sage_workspace_bytes(sage_shape s);
+
+/* Lays out the quantized operands of shape s inside ws (device memory,
+ * 256-byte aligned, at least sage_workspace_bytes(s) bytes) and fills *out.
+ * Host only; touches no device memory.
+ * Errors: INVALID_ARGUMENT (bad shape, out == NULL), WORKSPACE. */
+sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_quantized* out);
+
+/* The prepass ("Sage2 Blackwell Mainloop", Decision: K mean/smoothing, Q
+ * quantization, K subtract-mean quantization, V scale/FP8 quantization):
+ *   k_mean[b,h,d]  = (sum over 64-row tiles, in order, of the in-order FP32
+ *                     sum of K over the tile's rows) / N
+ *   per 32-row group of Q and per 64-row tile of K - k_mean:
+ *                    a = max |x|; scale = a/127; code = rne(x * (127/a))
+ *                    clamped to [-127, 127]
+ *   per channel of V over all N rows: a = max |v|; scale = a/448;
+ *                    code = E4M3(v * (448/a)), round to nearest even
+ *   (groups, tiles or channels with a < 2^-100 get scale 0 and zero codes).
+ * q, k, v share qz->shape.  Writes every field of *qz (including scratch).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                              const sage_quantized* qz, void* stream);
+
+/* The fused mainloop and epilogue ("State-Ownership Architecture Decision",
+ * Non-Negotiable Dataflow).  For every query row, over K/V tiles t = 0..T-1:
+ *   S = q_i8 . k_i8^T (exact int32);  t = S * (q_scale*k_scale*sm_scale*log2 e)
+ *   m' = max(m, max t); alpha = 2^(m - m'); RO *= alpha; d *= alpha
+ *   p = 448 * 2^(t - m') (keys >= N masked); d += sum p; P8 = E4M3(p)
+ *   RO += P8 . v_fp8 (FP32 accumulation, tile by tile in increasing order)
+ * then O = BF16((RO * (1/d)) * v_scale).  sm_scale must be finite and > 0
+ * (the usual choice is 1/sqrt(128)).  Reads only *qz's operands.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale,
+                                    const sage_bf16_out* o, void* stream);
+
+/* Whole path: carve ws, sage_quantize_qkv, then sage_attn_fwd_quantized, all
+ * on `stream`.  ws must hold sage_workspace_bytes(s) bytes, 256-byte aligned.
+ * Errors: as the calls above, and WORKSPACE. */
+sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                          sage_shape s, float sm_scale, const sage_bf16_out* o,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* sage_status_string(sage_status st);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* sage_last_error_message(void);
+
+/* SAGE_ABI_VERSION of the loaded library. */
+int32_t sage_abi_version(void);
+
+/* ---- test and inspection entry points (not on the hot path) ---- */
+
+/* The int32 Q.K^T sums the mainloop computes, produced by the mainloop's own
+ * tile routine, for every (b, h, query row < Nq, key < 64*T):
+ * s_out[((b*H + h)*Nq + r)*(64*T) + n].  Materialises an Nq-by-Nk tensor per
+ * head, so N <= 4096 is required.  Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* stream);
+
+/* The FP32 -> E4M3FN conversion the kernels use (round to nearest even), on n
+ * values; |x| must be below 464 for a finite code.  Errors: INVALID_ARGUMENT, HIP. */
+sage_status sage_debug_cvt_e4m3(const float* x, uint8_t* y, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_MI355X_H */

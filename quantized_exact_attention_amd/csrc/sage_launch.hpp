@@ -1,0 +1,86 @@
+// sage_launch.hpp -- kernel argument blocks and host launchers (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+struct StatsArgs {
+    const uint16_t* k; int64_t k_sb, k_sn, k_sh;
+    const uint16_t* v; int64_t v_sb, v_sn, v_sh;
+    int H, N, T;
+    int64_t units;
+    float* k_tile_sum;
+    float* v_tile_amax;
+};
+
+struct FinalizeArgs {
+    const float* k_tile_sum;
+    const float* v_tile_amax;
+    int T, N;
+    float* k_mean;
+    float* v_scale;
+    float* v_inv;
+};
+
+struct QuantQArgs {
+    const uint16_t* q; int64_t sb, sn, sh;
+    int H, N, G;
+    int64_t waves;
+    int8_t* q_i8;
+    float* q_scale;
+};
+
+struct QuantKArgs {
+    const uint16_t* k; int64_t sb, sn, sh;
+    int H, N, T;
+    int64_t waves;
+    const float* k_mean;
+    int8_t* k_i8;
+    float* k_scale;
+};
+
+struct QuantVArgs {
+    const uint16_t* v; int64_t sb, sn, sh;
+    int H, N, T;
+    const float* v_inv;
+    const float* v_scale;
+    uint8_t* v_fp8;
+};
+
+struct PrepassArgs {
+    int B, N, H, T, G;
+    const uint16_t* q; int64_t q_sb, q_sn, q_sh;
+    const uint16_t* k; int64_t k_sb, k_sn, k_sh;
+    const uint16_t* v; int64_t v_sb, v_sn, v_sh;
+    int8_t* q_i8; float* q_scale;
+    int8_t* k_i8; float* k_scale; float* k_mean;
+    uint8_t* v_fp8; float* v_scale;
+    float* k_tile_sum; float* v_tile_amax; float* v_inv;
+};
+
+struct MainloopArgs {
+    const int8_t* q_i8; const float* q_scale;
+    const int8_t* k_i8; const float* k_scale;
+    const uint8_t* v_fp8; const float* v_scale;
+    uint16_t* o; int64_t o_sb, o_sn, o_sh;
+    int B, N, H, T, G;
+    int n_qblk;          // workgroup Q blocks per (b, h)
+    int n_items;         // B * H * n_qblk
+    float c;             // sm_scale * log2(e), rounded to FP32
+};
+
+struct DebugQkArgs {
+    const int8_t* q_i8;
+    const int8_t* k_i8;
+    int32_t* s_out;
+    int B, N, H, T, G;
+};
+
+hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream);
+hipError_t launch_mainloop(const MainloopArgs& p, hipStream_t stream);
+hipError_t launch_debug_qk(const DebugQkArgs& p, hipStream_t stream);
+hipError_t launch_cvt_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t stream);
+
+}  // namespace sage

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: bit-exact on every quantized byte, every scale, the K mean and the int32
+QK sums; on the BF16 output, max |gpu - oracle| <= 2e-2 and cosine >= 0.9999
+over the compared rows.  Workloads: tiny, the tile-boundary sweep, mid, large
+and canonical (long-context, projection-strided).  Small workloads compare
+every row; large and canonical compare all quantized bytes in full and the
+output on sampled rows (the first group, the ragged last rows, random rows of
+every head), which the oracle computes one by one.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import layouts
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MIN_COS = 0.9999
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_exact_attention_amd as s
+    s._load()
+    return s
+
+
+@functools.lru_cache(maxsize=2)
+def _cpu_inputs(name):
+    return workloads.generate(workloads.by_name(name))
+
+
+@functools.lru_cache(maxsize=2)
+def _oracle_quant(name):
+    import oracle
+    inp = _cpu_inputs(name)
+    return oracle.quantize(inp.q, inp.k, inp.v)
+
+
+def _to_gpu(inp):
+    if inp.buffer is not None:
+        buf = inp.buffer.cuda()
+        B, N, H = inp.q.shape[:3]
+        views = [buf[:, :, i * H * 128:(i + 1) * H * 128].view(B, N, H, 128) for i in range(3)]
+        return views[0], views[1], views[2]
+    return inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+
+
+def _bits(x):
+    return np.asarray(x).view(np.uint32) if np.asarray(x).dtype == np.float32 else np.asarray(x)
+
+
+def _cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def _dec_bf16(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+ALL = ["tiny"] + ["sweep_n%d" % n for n in workloads.SWEEP_NS] + ["mid", "large", "canonical"]
+SMALL = ["tiny"] + ["sweep_n%d" % n for n in workloads.SWEEP_NS]
+
+
+# ------------------------------------------------------------------ codec --
+
+def test_cvt_e4m3_matches_oracle(sage):
+    import oracle
+    vals = oracle.e4m3_decode(np.arange(127)).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    rnd = rnd[np.isfinite(rnd) & (np.abs(rnd) < 464.0)]
+    x = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                        vals.astype(np.float32), rng.uniform(-463.9, 463.9, 500_000).astype(np.float32), rnd])
+    x = np.concatenate([x, -x, np.array([0.0, -0.0, 448.0, 460.0], np.float32)])
+    _log("cvt_e4m3: %d values" % x.size)
+    got = sage.debug_cvt_e4m3(torch.from_numpy(x).cuda()).cpu().numpy()
+    ref = oracle.e4m3_encode(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
+
+
+# -------------------------------------------------------- quantized bytes --
+
+@pytest.mark.parametrize("name", ALL)
+def test_quantized_bytes_bit_exact(sage, name):
+    _log("quant parity: %s" % name)
+    w = workloads.by_name(name)
+    q, k, v = _to_gpu(_cpu_inputs(name))
+    qz = sage.quantize_qkv(q, k, v)
+    torch.cuda.synchronize()
+    ref = _oracle_quant(name)
+    B, N, H = w.B, w.N, w.H
+    assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
+    assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    gq = layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gq, ref.q_i8), "q_i8 differs in %d bytes" % int((gq != ref.q_i8).sum())
+    gk = layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gk, ref.k_i8), "k_i8 differs in %d bytes" % int((gk != ref.k_i8).sum())
+    gv = layouts.v_logical(qz.v_fp8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gv, ref.v8), "v_fp8 differs in %d bytes" % int((gv != ref.v8).sum())
+
+
+# ------------------------------------------------------------- int32 QK --
+
+@pytest.mark.parametrize("name", SMALL + ["mid"])
+def test_qk_s32_bit_exact(sage, name):
+    import oracle
+    _log("qk_s32 parity: %s" % name)
+    q, k, v = _to_gpu(_cpu_inputs(name))
+    qz = sage.quantize_qkv(q, k, v)
+    s = sage.debug_qk_s32(qz)
+    torch.cuda.synchronize()
+    ref_q = _oracle_quant(name)
+    if name == "mid":
+        rows = [(0, 256), (qz.Nq - 128, qz.Nq)]
+    else:
+        rows = [(0, qz.Nq)]
+    for r0, r1 in rows:
+        ref = oracle.qk_s32(ref_q, r0, r1)
+        got = s[:, :, r0:r1].cpu().numpy()
+        assert np.array_equal(got, ref), "rows %d..%d: %d mismatches" % (r0, r1, int((got != ref).sum()))
+
+
+# -------------------------------------------------------------- attention --
+
+def _sample_rows(w, per_head_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(w.B):
+        for h in range(w.H):
+            rr = set(range(min(32, w.N)))                                   # first group
+            rr |= set(range(max(0, w.N - 50), w.N))                          # ragged last rows
+            rr |= set(rng.choice(w.N, min(per_head_random, w.N), replace=False).tolist())
+            rows += [(b, h, r) for r in sorted(rr)]
+    return np.array(rows, np.int64)
+
+
+def _attn_check(sage, name, rows=None, sm_scale=None):
+    import oracle
+    w = workloads.by_name(name)
+    q, k, v = _to_gpu(_cpu_inputs(name))
+    out = sage.attn_fwd(q, k, v, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    got_all = out.view(torch.int16).cpu().numpy().view(np.uint16)                   # [B,N,H,D]
+    ref_q = _oracle_quant(name)
+    if rows is None:
+        bb, hh, rr = np.meshgrid(np.arange(w.B), np.arange(w.H), np.arange(w.N), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), rr.ravel()], axis=1)
+    ref_bits, _ = oracle.attn_rows(ref_q, rows, sm_scale if sm_scale is not None else oracle.default_sm_scale())
+    got_bits = got_all[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got = _dec_bf16(got_bits).astype(np.float64)
+    ref = _dec_bf16(ref_bits).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    max_abs = float(np.max(np.abs(got - ref)))
+    cos = _cos(got, ref)
+    exact = float(np.mean(got_bits == ref_bits))
+    _log("attn %s: rows=%d max_abs=%.3g cos=%.7f bit-equal=%.3f" % (name, len(rows), max_abs, cos, exact))
+    assert max_abs <= MAX_ABS, max_abs
+    assert cos >= MIN_COS, cos
+    return out
+
+
+@pytest.mark.parametrize("name", SMALL + ["mid"])
+def test_attention_parity_all_rows(sage, name):
+    _attn_check(sage, name)
+
+
+@pytest.mark.parametrize("name,per_head", [("large", 48), ("canonical", 24)])
+def test_attention_parity_sampled_rows(sage, name, per_head):
+    w = workloads.by_name(name)
+    _attn_check(sage, name, rows=_sample_rows(w, per_head, seed=7))
+
+
+@pytest.mark.parametrize("sm_scale", [0.02, 0.3])
+def test_attention_parity_other_scales(sage, sm_scale):
+    _attn_check(sage, "sweep_n129", sm_scale=sm_scale)
+
+
+# ----------------------------------------------------- structural behaviour --
+
+def test_deterministic_and_two_call_path_identical(sage):
+    q, k, v = _to_gpu(_cpu_inputs("mid"))
+    a = sage.attn_fwd(q, k, v)
+    b = sage.attn_fwd(q, k, v)
+    qz = sage.quantize_qkv(q, k, v)
+    c = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_output_strides_and_untouched_memory(sage):
+    q, k, v = _to_gpu(_cpu_inputs("sweep_n129"))
+    ref = sage.attn_fwd(q, k, v)
+    B, N, H, D = q.shape
+    big = torch.full((B, N + 3, H + 2, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, 1:N + 1, 1:H + 1]
+    sage.attn_fwd(q, k, v, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(view.view(torch.int16), ref.view(torch.int16))
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, 1:N + 1, 1:H + 1] = False
+    assert torch.all(big[mask] == 7.0)
+
+
+def test_padding_rows_do_not_matter(sage):
+    inp = _cpu_inputs("sweep_n65")
+    q, k, v = _to_gpu(inp)
+    # views into GPU buffers whose rows N..N+69 hold large garbage values
+    q2 = workloads.with_padding_rows(q, 70)
+    k2 = workloads.with_padding_rows(k, 70, fill_seed=3)
+    v2 = workloads.with_padding_rows(v, 70, fill_seed=4)
+    assert q2.stride(1) == q.stride(1) and q2.data_ptr() != q.data_ptr()
+    a = sage.attn_fwd(q, k, v)
+    b = sage.attn_fwd(q2, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33])
+def test_degenerate_short_sequences(sage, n):
+    import oracle
+    w = workloads.Workload("short%d" % n, 1, n, 3, seed=500 + n)
+    inp = workloads.generate(w)
+    out = sage.attn_fwd(inp.q.cuda(), inp.k.cuda(), inp.v.cuda())
+    torch.cuda.synchronize()
+    _, ref_bits, _ = oracle.attention(inp.q, inp.k, inp.v)
+    got = _dec_bf16(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    ref = _dec_bf16(ref_bits).astype(np.float64)
+    assert np.max(np.abs(got - ref)) <= MAX_ABS
+    assert _cos(got, ref) >= MIN_COS
+
+
+def test_closed_form_v_ones_and_q_zero_on_gpu(sage):
+    inp = _cpu_inputs("tiny")
+    ones = torch.ones_like(inp.v).cuda()
+    o = sage.attn_fwd(inp.q.cuda(), inp.k.cuda(), ones).float().cpu().numpy()
+    assert np.max(np.abs(o - 1.0)) <= 2.0 ** -4 + 200 * 2.0 ** -10 / 448.0 + 2.0 ** -8
+    zeros = torch.zeros_like(inp.q).cuda()
+    o = sage.attn_fwd(zeros, inp.k.cuda(), inp.v.cuda()).float().cpu().numpy()
+    qz = _oracle_quant("tiny")
+    import oracle
+    dec = oracle.e4m3_decode(qz.v8.ravel()).reshape(qz.v8.shape).astype(np.float64)
+    mean = dec[:, :, :200].mean(axis=2) * qz.v_scale.astype(np.float64)
+    assert np.max(np.abs(o - mean[:, None])) <= 2.0 ** -7 * np.abs(mean).max() + 1e-6
