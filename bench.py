@@ -1,0 +1,193 @@
+"""Benchmark of the quantized-attention hot path on one MI355X.
+
+One step = the whole path on one batch of the long-context workload
+(B=1, N=37810, H=56, D=128, projection-strided BF16 NHD inputs): the
+quantization prepass (K mean, INT8 Q/K, FP8 V) followed by the fused
+INT8-QK / FP8-PV mainloop writing BF16 NHD output.  Inputs are resident in
+HBM before timing starts.  Prints ONE JSON line on stdout.
+
+  value       effective TOPS of the whole step: 4*N^2*H*D / step time
+  roofline    the mainloop kernel: effective ops / its average duration
+              (HIP events on the launch stream) against the MI355X dense
+              INT8/FP8 matrix peak of 5.0 POP/s
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+              (one head's prepass plus whole query rows of that head over
+              all keys), extrapolated to the full workload
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused mainloop ms & effective TOPS at N=37810,H=56,D=128; % MFMA peak"
+PEAK_TOPS = 5000.0          # MI355X dense INT8 / FP8 matrix peak, TOP/s
+HD = 128
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def effective_ops(B, N, H):
+    # per (query, key) pair: 128 INT8 multiply-adds for QK and 128 FP8
+    # multiply-adds for PV, two ops each
+    return 4.0 * B * N * N * H * HD
+
+
+def prepass_bytes(B, N, H):
+    T = -(-N // 64)
+    Nq = -(-N // 128) * 128
+    elems = B * N * H * HD
+    reads = 5 * 2 * elems                                # Q once, K and V twice (BF16)
+    writes = B * H * (Nq + 2 * T * 64) * HD              # INT8 Q, INT8 K, FP8 V
+    return reads + writes
+
+
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
+    """Time the oracle on one head: its prepass over all N rows, then whole
+    query rows (all N keys each) in batches until min_seconds have passed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    one = workloads.Workload("sample", 1, w.N, 1, seed=w.seed, layout="projection")
+    inp = workloads.generate(one)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    qz = oracle.quantize(inp.q, inp.k, inp.v)
+    t_prep = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows_done = 0
+    t_rows = 0.0
+    batch = 256
+    while t_rows < min_seconds and t_rows < max_seconds:
+        r = rng.choice(w.N, batch, replace=False)
+        rows = np.stack([np.zeros(batch, np.int64), np.zeros(batch, np.int64), r], axis=1)
+        t0 = time.perf_counter()
+        oracle.attn_rows(qz, rows)
+        dt = time.perf_counter() - t0
+        t_rows += dt
+        rows_done += batch
+        if dt < 2.0:
+            batch *= 2
+    per_row = t_rows / rows_done
+    est = w.B * w.H * (t_prep + per_row * w.N)
+    del torch
+    return {
+        "value": effective_ops(w.B, w.N, w.H) / est / 1e12,
+        "unit": "TOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("head 0 of the same workload: prepass over all %d rows (%.2f s) and %d whole query rows "
+                   "against all %d keys (%.2f s); extrapolated x%d heads to %.0f s for one step"
+                   % (w.N, t_prep, rows_done, w.N, t_rows, w.H, est)),
+        "est_step_s": est,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="canonical")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X (run with --gpus 1); "
+              "how it would shard over several GPUs is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_exact_attention_amd as sage
+    import workloads
+
+    w = workloads.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating %s B=%d N=%d H=%d (%s)" % (w.name, w.B, w.N, w.H, w.layout))
+    inp = workloads.generate(w)
+    if inp.buffer is not None:
+        buf = inp.buffer.to(dev)
+        q, k, v = [buf[:, :, i * w.H * HD:(i + 1) * w.H * HD].view(w.B, w.N, w.H, HD) for i in range(3)]
+    else:
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    del inp
+    out = torch.empty((w.B, w.N, w.H, HD), dtype=torch.bfloat16, device=dev)
+    qz = sage.Quantized(w.B, w.N, w.H, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # warmup: the same calls as the timed steps
+    for _ in range(args.warmup):
+        sage.quantize_qkv(q, k, v, into=qz)
+        sage.attn_fwd_quantized(qz, out=out)
+    torch.cuda.synchronize(dev)
+    log("bench: warmup done (%d steps)" % args.warmup)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sage.quantize_qkv(q, k, v, into=qz)
+        ev[i][1].record(stream)
+        sage.attn_fwd_quantized(qz, out=out)
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    total_ms = t_start.elapsed_time(t_end)
+    prep_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    main_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_per_step = total_ms / args.steps
+    ops = effective_ops(w.B, w.N, w.H)
+    main_avg = sum(main_ms) / len(main_ms)
+    prep_avg = sum(prep_ms) / len(prep_ms)
+    main_sorted = sorted(main_ms)
+    log("bench: step %.3f ms  mainloop avg %.3f ms (min %.3f, p50 %.3f, max %.3f)  prepass %.3f ms"
+        % (ms_per_step, main_avg, main_sorted[0], main_sorted[len(main_sorted) // 2], main_sorted[-1], prep_avg))
+    achieved = ops / (main_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": ops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8e4m3 (fp32 softmax/accumulate, bf16 in/out)",
+        "data": "synthetic (seeded; Q,V~N(0,1), K~N(0,1)+per-channel N(0,3) offset; BF16)",
+        "config": {"workload": "%s: B=%d N=%d H=%d D=128, non-causal, %s BF16 NHD inputs, contiguous BF16 NHD output"
+                               % (w.name, w.B, w.N, w.H, "projection-strided" if w.layout == "projection"
+                                  else "contiguous"),
+                   "global_batch": w.B, "seq_len": w.N, "heads": w.H, "head_dim": HD, "parallelism": "single GPU"},
+        "mainloop_ms": main_avg,
+        "mainloop_ms_p50": main_sorted[len(main_sorted) // 2],
+        "mainloop_tops": achieved,
+        "prepass_ms": prep_avg,
+        "prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (prep_avg * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_TOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        cb = cpu_baseline(w)
+        cb.pop("est_step_s")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

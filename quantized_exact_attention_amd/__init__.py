@@ -200,13 +200,21 @@ class Quantized:
         return self._view("v_scale", _torch().float32, self.B * self.H * HEAD_DIM).view(self.B, self.H, HEAD_DIM)
 
 
-def quantize_qkv(q, k, v, workspace=None) -> Quantized:
-    """The prepass: K mean, INT8 Q/K and FP8 V with their scales."""
+def quantize_qkv(q, k, v, workspace=None, into: Quantized = None) -> Quantized:
+    """The prepass: K mean, INT8 Q/K and FP8 V with their scales.
+
+    With ``into``, the operands are rewritten in that object's workspace
+    (same shape required) and nothing is allocated."""
     dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
     if not (q.shape == k.shape == v.shape):
         raise SageError("q, k, v shapes differ")
     B, N, H, _ = q.shape
-    qz = Quantized(B, N, H, q.device, workspace)
+    if into is not None:
+        if (into.B, into.N, into.H) != (B, N, H):
+            raise SageError("into has shape %s, inputs %s" % ((into.B, into.N, into.H), (B, N, H)))
+        qz = into
+    else:
+        qz = Quantized(B, N, H, q.device, workspace)
     _check(_load().sage_quantize_qkv(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                                      ctypes.byref(qz.c), _stream_ptr(q)))
     qz._inputs = (q, k, v)

@@ -33,7 +33,6 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStageBytes = 2 * kTileBytes;       // K tile + V tile
 constexpr float kLog2Of448 = 8.8073549220576041f;  // log2(448)
 
 // Bijection from dispatch order to work items such that the items dispatched
@@ -66,17 +65,281 @@ __device__ __forceinline__ int key_of(int blk, int r, int lane) {
     return 32 * blk + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// PV of one wave against one staged V tile: ro[db] += V^T(rows 32db..) . P^T,
+// accumulated straight into the FP32 output rows.
+__device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int lane, v16f (&ro)[4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const v4i lo = *(const v4i*)(vtile + ((db * 2 + 0) * 64 + lane) * 16);
+        const v4i hi = *(const v4i*)(vtile + ((db * 2 + 1) * 64 + lane) * 16);
+        const v8i vf = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        ro[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, ro[db], 0, 0, 0, 127, 0, 127);
+    }
+}
+
+// Online softmax of one tile for this lane's query row (32 of the tile's keys
+// here, the other 32 on lane l^32): max update on the exact int32 sums (the
+// score scale sj is positive, so the largest sum gives the largest score),
+// alpha = 2^(m - m_new), p = 448 * 2^(t - m_new) with 448 folded into the
+// exponent offset, this lane's part of the denominator, and the FP8 codes
+// packed in the B-operand order of the PV instruction.  kLast masks keys at
+// or beyond `tail` in the final, partial tile.
+template <bool kLast>
+__device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int tail, int lane, float& m,
+                                             float& dpart, float& alpha, v8i& pk) {
+    if (kLast) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (key_of(0, r, lane) >= tail) s0[r] = INT32_MIN;
+            if (key_of(1, r, lane) >= tail) s1[r] = INT32_MIN;
+        }
+    }
+    int ma = max(s0[0], s0[1]);
+    int mb = max(s1[0], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+        ma = max(ma, max(s0[r], s0[r + 1]));
+        mb = max(mb, max(s1[r], s1[r + 1]));
+    }
+    const int mx = halves_max(max(ma, mb));
+    const float m_new = fmaxf(m, (float)mx * sj);
+    alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    const float off = kLog2Of448 - m_new;
+    float p[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s0[r], sj, off));
+        p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s1[r], sj, off));
+    }
+    if (kLast) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (key_of(0, r, lane) >= tail) p[r] = 0.0f;
+            if (key_of(1, r, lane) >= tail) p[16 + r] = 0.0f;
+        }
+    }
+    float d0 = dpart * alpha, d1 = p[1], d2 = p[2], d3 = p[3];
+    d0 += p[0];
+#pragma unroll
+    for (int r = 4; r < 32; r += 4) {
+        d0 += p[r];
+        d1 += p[r + 1];
+        d2 += p[r + 2];
+        d3 += p[r + 3];
+    }
+    dpart = (d0 + d1) + (d2 + d3);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], __float_as_int(p[4 * v]));
+        pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
+    }
+}
+
+__device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ro[db][r] *= alpha;
+}
+
+// LDS rings: K tiles in 3 slots, V tiles in 4 slots, filled straight from
+// global memory by global_load_lds_dwordx4 (no VGPR staging).  In iteration j
+// a wave issues PV of tile j-1 (V slot (j-1)%4), the softmax of tile j
+// (scores computed in the previous iteration) and QK of tile j+1 (K slot
+// (j+1)%3), while the block's loads of K(j+3) and V(j+2) are in flight; the
+// loads issued one iteration earlier are waited for before the barrier that
+// ends the iteration.  RO receives every tile's PV in increasing tile order,
+// each after the rescale by that tile's alpha.
+constexpr int kKSlots = 3;
+constexpr int kVSlots = 4;
+
+// Each wave copies its 1 KiB share of an 8 KiB tile from global memory into
+// an LDS slot; lane l's 16 bytes land at the wave's base + 16*l (LDS address
+// taken from M0, which is restored afterwards; the instruction reads it at
+// issue).  Issued as inline assembly so that the compiler does not
+// make every later LDS read wait for these loads: the instruction writes no
+// VGPR, and the only consumer synchronisation is the explicit vmcnt wait
+// before the block barrier that publishes the tile.
+__device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, int wave, int lane) {
+    const int8_t* src = gtile + (wave * 64 + lane) * 16;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(slot + wave * 1024));
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(src), "s"(dst)
+        : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8): wait until at most 2 / 0 vector-memory
+// operations of this wave are outstanding, without waiting on the others.
+constexpr int kWaitVm2 = 0x0F72;
+constexpr int kWaitVm0 = 0x0F70;
+
+// Workgroup barrier without the memory fence of __syncthreads() (whose
+// vmcnt(0) would also wait for the tile loads still meant to be in flight).
+// The loop reaches it only after every LDS read of the iteration has been
+// consumed and after the explicit wait for the tiles the next iteration
+// reads; the memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wave-uniform loads of data the kernel never writes go through the scalar
+// cache (constant address space), so they do not join the vector-memory
+// counter that tracks the tile loads in flight.
+typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+
+#define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Operand reads from a staged tile; `lane_base` is the slot address plus
+// 16*lane, so every read of an iteration is one base register plus an
+// immediate offset.
+__device__ __forceinline__ v8i load_vfrag(const int8_t* lane_base, int db) {
+    const v4i lo = *(const v4i*)(lane_base + (db * 2 + 0) * 1024);
+    const v4i hi = *(const v4i*)(lane_base + (db * 2 + 1) * 1024);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ v4i load_kfrag(const int8_t* lane_base, int blk, int kk) {
+    return *(const v4i*)(lane_base + (blk * 4 + kk) * 1024);
+}
+
+__device__ __forceinline__ v16f mfma_pv(const v8i& vf, const v8i& pk, const v16f& acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, acc, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ v16i mfma_qk(const v4i& kf, const v4i& qf, const v16i& acc) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf, acc, 0, 0, 0);
+}
+
+// One steady-state iteration for tile j (not the last): PV of tile j-1, the
+// softmax of tile j and QK of tile j+1, written as a fixed sequence in which
+// each matrix instruction is followed by a slice of the softmax's vector
+// work (fenced so the compiler keeps the order), and each LDS operand read
+// is issued one step before its use.  One wavefront thereby keeps its matrix
+// and vector pipes busy together.  Numerically identical to softmax_tile
+// followed by pv_tile / qk_tile.
+__device__ __forceinline__ void steady_iteration(const int8_t* vtile_prev, const int8_t* ktile_next,
+                                                 const v4i (&qf)[4], int lane, float sj, float& m, float& dpart,
+                                                 float& alpha, v8i& pk, v16i& s0, v16i& s1, v16f (&ro)[4]) {
+    const v8i pprev = pk;
+    const int8_t* vbase = vtile_prev + lane * 16;
+    const int8_t* kbase = ktile_next + lane * 16;
+    v8i vf0 = load_vfrag(vbase, 0);
+    v8i vf1 = load_vfrag(vbase, 1);
+    ro[0] = mfma_pv(vf0, pprev, ro[0]);
+    SAGE_FENCE();
+    int ma = max(s0[0], s0[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) ma = max(ma, max(s0[r], s0[r + 1]));
+    vf0 = load_vfrag(vbase, 2);
+    ro[1] = mfma_pv(vf1, pprev, ro[1]);
+    SAGE_FENCE();
+    int mb = max(s1[0], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mb = max(mb, max(s1[r], s1[r + 1]));
+    const int mx = halves_max(max(ma, mb));
+    const float m_new = fmaxf(m, (float)mx * sj);
+    alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    const float off = kLog2Of448 - m_new;
+    vf1 = load_vfrag(vbase, 3);
+    ro[2] = mfma_pv(vf0, pprev, ro[2]);
+    SAGE_FENCE();
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_fmaf((float)s0[r], sj, off);
+    v4i ka = load_kfrag(kbase, 0, 0);
+    v4i kb = load_kfrag(kbase, 1, 0);
+    ro[3] = mfma_pv(vf1, pprev, ro[3]);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 8; r < 16; ++r) x[r] = __builtin_fmaf((float)s0[r], sj, off);
+    v16i n0 = mfma_qk(ka, qf[0], v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});
+    ka = load_kfrag(kbase, 0, 1);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[16 + r] = __builtin_fmaf((float)s1[r], sj, off);
+    v16i n1 = mfma_qk(kb, qf[0], v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});
+    kb = load_kfrag(kbase, 1, 1);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 8; r < 16; ++r) x[16 + r] = __builtin_fmaf((float)s1[r], sj, off);
+    n0 = mfma_qk(ka, qf[1], n0);
+    ka = load_kfrag(kbase, 0, 2);
+    SAGE_FENCE();
+    float p[32];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+    n1 = mfma_qk(kb, qf[1], n1);
+    kb = load_kfrag(kbase, 1, 2);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 8; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+    n0 = mfma_qk(ka, qf[2], n0);
+    ka = load_kfrag(kbase, 0, 3);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 16; r < 24; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+    n1 = mfma_qk(kb, qf[2], n1);
+    kb = load_kfrag(kbase, 1, 3);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 24; r < 32; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+    n0 = mfma_qk(ka, qf[3], n0);
+    SAGE_FENCE();
+    float d0 = dpart * alpha, d1 = p[1], d2 = p[2], d3 = p[3];
+    d0 += p[0];
+#pragma unroll
+    for (int r = 4; r < 16; r += 4) {
+        d0 += p[r];
+        d1 += p[r + 1];
+        d2 += p[r + 2];
+        d3 += p[r + 3];
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], __float_as_int(p[4 * v]));
+        pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
+    }
+    n1 = mfma_qk(kb, qf[3], n1);
+    SAGE_FENCE();
+#pragma unroll
+    for (int r = 16; r < 32; r += 4) {
+        d0 += p[r];
+        d1 += p[r + 1];
+        d2 += p[r + 2];
+        d3 += p[r + 3];
+    }
+    dpart = (d0 + d1) + (d2 + d3);
+#pragma unroll
+    for (int v = 4; v < 8; ++v) {
+        const int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], __float_as_int(p[4 * v]));
+        pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
+    }
+    s0 = n0;
+    s1 = n1;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
-    __shared__ __attribute__((aligned(16))) int8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
+    __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = item / a.n_qblk;
     const int qb = item - bh * a.n_qblk;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int g = qb * kWaves + wave;
     const bool active = g < a.G && g * kQG < a.N;
+    const int T = a.T;
+    const int tid16 = threadIdx.x * 16;
 
     v4i qf[4];
     float qs = 0.0f;
@@ -90,15 +353,25 @@ __global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
         for (int kk = 0; kk < 4; ++kk) qf[kk] = v4i{0, 0, 0, 0};
     }
 
-    const int8_t* kg = a.k_i8 + (int64_t)bh * a.T * kTileBytes + threadIdx.x * 16;
-    const int8_t* vg = (const int8_t*)a.v_fp8 + (int64_t)bh * a.T * kTileBytes + threadIdx.x * 16;
-    const float* ksc = a.k_scale + (int64_t)bh * a.T;
+    const int8_t* kg = a.k_i8 + (int64_t)bh * T * kTileBytes;
+    const int8_t* vg = (const int8_t*)a.v_fp8 + (int64_t)bh * T * kTileBytes;
+    const const_f32_ptr ksc = (const_f32_ptr)(a.k_scale + (int64_t)bh * T);
+    const float c = a.c;
 
-    v4i kr = *(const v4i*)kg;
-    v4i vr = *(const v4i*)vg;
-    *(v4i*)(lds + threadIdx.x * 16) = kr;
-    *(v4i*)(lds + kTileBytes + threadIdx.x * 16) = vr;
+    // Prologue: K(0..2) and V(0..1) in flight to LDS; V slot 3 zeroed so the
+    // PV of "tile -1" in iteration 0 adds exact zeros.  Loads past the last
+    // tile are clamped to it and land in slots that are never read again.
+    tile_to_lds(kg, lds_k, wave, lane);
+    tile_to_lds(vg, lds_v, wave, lane);
+    tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, wave, lane);
+    tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, wave, lane);
+    tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, wave, lane);
+    *(v4i*)(lds_v + 3 * kTileBytes + tid16) = v4i{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    v16i s0, s1;
+    if (active) qk_tile(lds_k, qf, lane, s0, s1);
+    __syncthreads();   // K slot 0 is refilled in iteration 0
 
     float m = -INFINITY;
     float dpart = 0.0f;    // this lane's share of the row denominator
@@ -107,85 +380,50 @@ __global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ro[db][r] = 0.0f;
+    v8i pprev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
-    const int tail = a.N - (a.T - 1) * kBK;   // valid keys in the last tile, 1..64
-
-    for (int j = 0; j < a.T; ++j) {
-        const int8_t* st = lds + (j & 1) * kStageBytes;
-        const bool more = j + 1 < a.T;
-        if (more) {
-            kr = *(const v4i*)(kg + (int64_t)(j + 1) * kTileBytes);
-            vr = *(const v4i*)(vg + (int64_t)(j + 1) * kTileBytes);
-        }
+    // alpha of the previous tile, applied to RO just before that tile's PV
+    float alpha_prev = 1.0f;
+    bool pending = false;
+    // Ring slots by role, rotated each iteration: kq holds K(j+1) for this
+    // iteration's QK and kf receives K(j+3); vp holds V(j-1) for this
+    // iteration's PV and vf receives V(j+2).
+    int8_t* kq = lds_k + kTileBytes;
+    int8_t* kn = lds_k + 2 * kTileBytes;
+    int8_t* kf = lds_k;
+    int8_t* vp = lds_v + 3 * kTileBytes;
+    int8_t* v0 = lds_v;
+    int8_t* v1 = lds_v + kTileBytes;
+    int8_t* vf = lds_v + 2 * kTileBytes;
+    for (int j = 0; j < T - 1; ++j) {
+        const float ksj = ksc[j];
+        tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, wave, lane);
+        tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, wave, lane);
         if (active) {
-            v16i s0, s1;
-            qk_tile(st, qf, lane, s0, s1);
-            const bool last = (j == a.T - 1) && tail < kBK;
-            if (last) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if (key_of(0, r, lane) >= tail) s0[r] = INT32_MIN;
-                    if (key_of(1, r, lane) >= tail) s1[r] = INT32_MIN;
-                }
-            }
-            // Row max on the exact int32 sums (the score scale is positive).
-            int mx = max(s0[0], s1[0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = max(mx, max(s0[r], s1[r]));
-            mx = max(mx, other_half(mx));
-            const float sj = (qs * ksc[j]) * a.c;
-            const float m_new = fmaxf(m, (float)mx * sj);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            if (__any(m_new != m)) {
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) ro[db][r] *= alpha;
-            }
-            dpart *= alpha;
-            m = m_new;
-            // p = 448 * 2^(t - m) with 448 folded into the exponent offset.
-            const float off = kLog2Of448 - m_new;
-            float p[32];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s0[r], sj, off));
-                p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s1[r], sj, off));
-            }
-            if (last) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if (key_of(0, r, lane) >= tail) p[r] = 0.0f;
-                    if (key_of(1, r, lane) >= tail) p[16 + r] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 32; ++r) dpart += p[r];
-            v8i pk;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], 0);
-                pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
-            }
-            const int8_t* vt = st + kTileBytes;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const v4i lo = *(const v4i*)(vt + ((db * 2 + 0) * 64 + lane) * 16);
-                const v4i hi = *(const v4i*)(vt + ((db * 2 + 1) * 64 + lane) * 16);
-                const v8i vf = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                ro[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, ro[db], 0, 0, 0, 127, 0, 127);
-            }
+            if (pending) rescale(ro, alpha_prev);
+            steady_iteration(vp, kq, qf, lane, (qs * ksj) * c, m, dpart, alpha_prev, pprev, s0, s1, ro);
+            pending = __any(alpha_prev != 1.0f);
         }
-        if (more) {
-            int8_t* nx = lds + ((j + 1) & 1) * kStageBytes;
-            *(v4i*)(nx + threadIdx.x * 16) = kr;
-            *(v4i*)(nx + kTileBytes + threadIdx.x * 16) = vr;
-        }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);   // K(j+2), V(j+1) have landed
+        block_barrier();
+        int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
+        t = vp;  vp = v0;  v0 = v1;  v1 = vf;  vf = t;
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     if (!active) return;
-    const float dtot = dpart + other_half(dpart);
+    {
+        const int j = T - 1;
+        if (pending) rescale(ro, alpha_prev);
+        pv_tile(vp, pprev, lane, ro);                // V(T-2), or zeros when T == 1
+        float alpha;
+        v8i pk;
+        softmax_tile<true>(s0, s1, (qs * ksc[j]) * c, a.N - j * kBK, lane, m, dpart, alpha, pk);
+        if (__any(alpha != 1.0f)) rescale(ro, alpha);
+        pv_tile(v0, pk, lane, ro);                   // V(T-1)
+    }
+
+    const float dtot = halves_sum(dpart);
     const float rcp = 1.0f / dtot;
     const int n = g * kQG + (lane & 31);
     if (n >= a.N) return;

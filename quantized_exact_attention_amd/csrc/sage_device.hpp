@@ -55,8 +55,31 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Value held by lane l^32 (the other half of the wave).
-__device__ __forceinline__ float other_half(float v) { return __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ int other_half(int v) { return __shfl_xor(v, 32, 64); }
+// Maximum of the 32 int32 values of two accumulator tiles (two chains, so
+// the compiler can form three-input maxima).  Kept in plain C++: the inputs
+// are matrix-instruction results, and only compiler-visible code gets the
+// wait states the hardware needs before reading them.
+__device__ __forceinline__ int max_of_32(const v16i& s0, const v16i& s1) {
+    int ma = max(s0[0], s0[1]);
+    int mb = max(s1[0], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+        ma = max(ma, max(s0[r], s0[r + 1]));
+        mb = max(mb, max(s1[r], s1[r + 1]));
+    }
+    return max(ma, mb);
+}
+
+// Combine a value across the two 32-lane halves of the wave without an LDS
+// round trip: v_permlane32_swap(x, x) yields, on every lane l, the values of
+// lanes l%32 and l%32 + 32, so both halves get bit-identical results.
+__device__ __forceinline__ int halves_max(int v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace sage
