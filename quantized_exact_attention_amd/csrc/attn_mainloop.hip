@@ -10,19 +10,21 @@
 // accumulate_d -> RS_32_to_8 -> PV, with private RS, RS_f8, RO, m and d.
 //
 // gfx950 design (not the pages' GB10 one):
-//   * A workgroup of 8 wavefronts owns 256 query rows of one (b, h); wave w
-//     owns the 32-row group g = 8*qb + w, so its Q scale is wave-uniform.
+//   * A workgroup of kMainloopWaves (4) wavefronts owns 128 query rows of one
+//     (b, h); wave w owns the 32-row group g = 4*qb + w, so its Q scale is
+//     wave-uniform.  Two workgroups share a CU (two waves per SIMD) and
+//     synchronise independently of each other.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8: lane l then holds 32 keys of the single query
 //     row l%32 (lanes l and l^32 share a row), so the row max and sum are
 //     in-lane plus one exchange with lane l^32, and the FP8 probabilities
 //     are already in the B-operand layout of the PV instruction.
-//   * PV is O^T = V^T . P^T with v_mfma_scale_f32_32x32x64_f8f6f4 (scales
-//     1.0), accumulating straight into the FP32 RO rows after the alpha
+//   * PV is O^T = V^T . P^T with v_mfma_scale_f32_32x32x64_f8f6f4 (block
+//     scales 1.0), accumulating straight into the FP32 RO rows after the alpha
 //     rescale, tile by tile in increasing order.
-//   * K and V tiles (8 KiB each, already in operand order) are double
-//     buffered in LDS; the next tile's 16-byte global loads are in flight
-//     while the current tile is computed.
+//   * K and V tiles (8 KiB each, already in operand order) stream through
+//     LDS rings filled by direct global-to-LDS loads issued two to three
+//     tiles ahead of their use.
 //   * The workgroup-to-(b, h, Q block) map keeps the workgroups that one XCD
 //     runs on the same head, so that head's K/V stream is shared in its L2.
 #include "sage_device.hpp"
@@ -31,8 +33,11 @@
 namespace sage {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = kMainloopWaves;
 constexpr int kThreads = kWaves * 64;
+// 1 KiB DMA instructions per wave per 8 KiB tile
+constexpr int kTileLoads = kTileBytes / (kWaves * 1024);
+static_assert(kTileLoads * kWaves * 1024 == kTileBytes, "tile split");
 constexpr float kLog2Of448 = 8.8073549220576041f;  // log2(448)
 
 // Bijection from dispatch order to work items such that the items dispatched
@@ -65,6 +70,11 @@ __device__ __forceinline__ int key_of(int blk, int r, int lane) {
     return 32 * blk + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// E4M3 x E4M3 -> FP32, 32x32x64, both block scales 1.0 (E8M0 127).
+__device__ __forceinline__ v16f mfma_pv(const v8i& vf, const v8i& pk, const v16f& acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, acc, 0, 0, 0, 127, 0, 127);
+}
+
 // PV of one wave against one staged V tile: ro[db] += V^T(rows 32db..) . P^T,
 // accumulated straight into the FP32 output rows.
 __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int lane, v16f (&ro)[4]) {
@@ -73,7 +83,7 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
         const v4i lo = *(const v4i*)(vtile + ((db * 2 + 0) * 64 + lane) * 16);
         const v4i hi = *(const v4i*)(vtile + ((db * 2 + 1) * 64 + lane) * 16);
         const v8i vf = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        ro[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, ro[db], 0, 0, 0, 127, 0, 127);
+        ro[db] = mfma_pv(vf, pk, ro[db]);
     }
 }
 
@@ -162,24 +172,29 @@ constexpr int kVSlots = 4;
 // VGPR, and the only consumer synchronisation is the explicit vmcnt wait
 // before the block barrier that publishes the tile.
 __device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, int wave, int lane) {
-    const int8_t* src = gtile + (wave * 64 + lane) * 16;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(slot + wave * 1024));
-    uint32_t saved_m0;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved_m0)
-        : "v"(src), "s"(dst)
-        : "memory");
+#pragma unroll
+    for (int i = 0; i < kTileLoads; ++i) {
+        const int part = wave * kTileLoads + i;
+        const int8_t* src = gtile + (part * 64 + lane) * 16;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(slot + part * 1024));
+        uint32_t saved_m0;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %2\n\t"
+            "global_load_lds_dwordx4 %1, off\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "v"(src), "s"(dst)
+            : "memory");
+    }
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4, lgkmcnt 11:8): wait until at most 2 / 0 vector-memory
 // operations of this wave are outstanding, without waiting on the others.
-constexpr int kWaitVm2 = 0x0F72;
 constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVmIter = 0x0F70 | (2 * kTileLoads);
+static_assert(2 * kTileLoads < 16, "vmcnt field");
 
 // Workgroup barrier without the memory fence of __syncthreads() (whose
 // vmcnt(0) would also wait for the tile loads still meant to be in flight).
@@ -209,9 +224,6 @@ __device__ __forceinline__ v4i load_kfrag(const int8_t* lane_base, int blk, int 
     return *(const v4i*)(lane_base + (blk * 4 + kk) * 1024);
 }
 
-__device__ __forceinline__ v16f mfma_pv(const v8i& vf, const v8i& pk, const v16f& acc) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, acc, 0, 0, 0, 127, 0, 127);
-}
 
 __device__ __forceinline__ v16i mfma_qk(const v4i& kf, const v4i& qf, const v16i& acc) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf, acc, 0, 0, 0);
@@ -326,7 +338,7 @@ __device__ __forceinline__ void steady_iteration(const int8_t* vtile_prev, const
     s1 = n1;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(MainloopArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
     __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
 
@@ -366,7 +378,9 @@ __global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
     tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, wave, lane);
     tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, wave, lane);
     tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, wave, lane);
-    *(v4i*)(lds_v + 3 * kTileBytes + tid16) = v4i{0, 0, 0, 0};
+    #pragma unroll
+    for (int i = 0; i < kTileLoads; ++i)
+        *(v4i*)(lds_v + 3 * kTileBytes + i * kThreads * 16 + tid16) = v4i{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     v16i s0, s1;
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 1) void mainloop_kernel(MainloopArgs a) {
             steady_iteration(vp, kq, qf, lane, (qs * ksj) * c, m, dpart, alpha_prev, pprev, s0, s1, ro);
             pending = __any(alpha_prev != 1.0f);
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);   // K(j+2), V(j+1) have landed
+        __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
         block_barrier();
         int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
         t = vp;  vp = v0;  v0 = v1;  v1 = vf;  vf = t;

@@ -209,7 +209,7 @@ sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, co
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.o = (uint16_t*)o->data; p.o_sb = o->stride_b; p.o_sn = o->stride_n; p.o_sh = o->stride_h;
     p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
-    p.n_qblk = (int)((d.G + 7) / 8);
+    p.n_qblk = (int)((d.G + sage::kMainloopWaves - 1) / sage::kMainloopWaves);
     const int64_t items = d.B * d.H * p.n_qblk;
     if (items > 0x7fffffff) return fail(SAGE_ERR_UNSUPPORTED, "too many work items");
     p.n_items = (int)items;

@@ -60,6 +60,9 @@ struct PrepassArgs {
     float* k_tile_sum; float* v_tile_amax; float* v_inv;
 };
 
+// Query groups (32 rows, one wavefront each) per mainloop workgroup.
+constexpr int kMainloopWaves = 4;
+
 struct MainloopArgs {
     const int8_t* q_i8; const float* q_scale;
     const int8_t* k_i8; const float* k_scale;
