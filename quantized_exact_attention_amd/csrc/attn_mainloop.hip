@@ -49,12 +49,22 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return base + slot;
 }
 
+// Score accumulators start at the bit pattern of 1.5 * 2^23 instead of 0.
+// Every |S| <= 128 * 127 * 127 < 2^22, so the int32 result 0x4B400000 + S is
+// the FP32 number 1.5 * 2^23 + S (fixed exponent, S in the mantissa): one
+// exact FP32 subtraction gives float(S) without a conversion instruction,
+// and the integer maximum of the biased words is the biased maximum of S.
+constexpr int kScoreBias = 0x4B400000;
+constexpr float kScoreBiasF = 12582912.0f;
+
+__device__ __forceinline__ float unbias(int s) { return __int_as_float(s) - kScoreBiasF; }
+
 // QK of one wave against one staged K tile: s0 = S^T for keys 0..31, s1 for
 // keys 32..63 (register r of lane l: key 8*(r/4) + 4*(l/32) + r%4 of its
-// block, query row l%32 of the wave's group).  Exact int32.
+// block, query row l%32 of the wave's group), exact int32 plus `init`.
 __device__ __forceinline__ void qk_tile(const int8_t* ktile, const v4i (&qf)[4], int lane,
-                                        v16i& s0, v16i& s1) {
-    s0 = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                                        v16i& s0, v16i& s1, int init) {
+    s0 = v16i{init, init, init, init, init, init, init, init, init, init, init, init, init, init, init, init};
     s1 = s0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -88,8 +98,9 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
 }
 
 // Online softmax of one tile for this lane's query row (32 of the tile's keys
-// here, the other 32 on lane l^32): max update on the exact int32 sums (the
-// score scale sj is positive, so the largest sum gives the largest score),
+// here, the other 32 on lane l^32), on biased sums (kScoreBias): max update on
+// the exact int32 sums (the score scale sj is positive, so the largest sum
+// gives the largest score),
 // alpha = 2^(m - m_new), p = 448 * 2^(t - m_new) with 448 folded into the
 // exponent offset, this lane's part of the denominator, and the FP8 codes
 // packed in the B-operand order of the PV instruction.  kLast masks keys at
@@ -108,10 +119,10 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
     int mb = max(s1[0], s1[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) {
-        ma = max(ma, max(s0[r], s0[r + 1]));
-        mb = max(mb, max(s1[r], s1[r + 1]));
+        ma = max(max(ma, s0[r]), s0[r + 1]);
+        mb = max(max(mb, s1[r]), s1[r + 1]);
     }
-    const int mx = halves_max(max(ma, mb));
+    const int mx = halves_max(max(ma, mb)) - kScoreBias;
     const float m_new = fmaxf(m, (float)mx * sj);
     alpha = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
@@ -119,8 +130,8 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
     float p[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s0[r], sj, off));
-        p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s1[r], sj, off));
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s0[r]), sj, off));
+        p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s1[r]), sj, off));
     }
     if (kLast) {
 #pragma unroll
@@ -233,55 +244,57 @@ __device__ __forceinline__ v16i mfma_qk(const v4i& kf, const v4i& qf, const v16i
 // softmax of tile j and QK of tile j+1, written as a fixed sequence in which
 // each matrix instruction is followed by a slice of the softmax's vector
 // work (fenced so the compiler keeps the order), and each LDS operand read
-// is issued one step before its use.  One wavefront thereby keeps its matrix
-// and vector pipes busy together.  Numerically identical to softmax_tile
-// followed by pv_tile / qk_tile.
+// is issued at least one step before its use (the first two V operands of
+// the next iteration at the end of this one, in va/vb).  One wavefront
+// thereby keeps its matrix and vector pipes busy together.  `bias` holds
+// kScoreBias in every register, the initial QK accumulator.  Numerically
+// identical to softmax_tile followed by pv_tile / qk_tile.
 __device__ __forceinline__ void steady_iteration(const int8_t* vtile_prev, const int8_t* ktile_next,
+                                                 const int8_t* vtile_after, v8i& va, v8i& vb,
                                                  const v4i (&qf)[4], int lane, float sj, float& m, float& dpart,
-                                                 float& alpha, v8i& pk, v16i& s0, v16i& s1, v16f (&ro)[4]) {
+                                                 float& alpha, v8i& pk, v16i& s0, v16i& s1, v16f (&ro)[4],
+                                                 const v16i& bias) {
     const v8i pprev = pk;
     const int8_t* vbase = vtile_prev + lane * 16;
     const int8_t* kbase = ktile_next + lane * 16;
-    v8i vf0 = load_vfrag(vbase, 0);
-    v8i vf1 = load_vfrag(vbase, 1);
-    ro[0] = mfma_pv(vf0, pprev, ro[0]);
+    v8i vf0 = load_vfrag(vbase, 2);
+    v8i vf1 = load_vfrag(vbase, 3);
+    ro[0] = mfma_pv(va, pprev, ro[0]);
     SAGE_FENCE();
     int ma = max(s0[0], s0[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) ma = max(ma, max(s0[r], s0[r + 1]));
-    vf0 = load_vfrag(vbase, 2);
-    ro[1] = mfma_pv(vf1, pprev, ro[1]);
+    for (int r = 2; r < 16; r += 2) ma = max(max(ma, s0[r]), s0[r + 1]);
+    ro[1] = mfma_pv(vb, pprev, ro[1]);
     SAGE_FENCE();
     int mb = max(s1[0], s1[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mb = max(mb, max(s1[r], s1[r + 1]));
-    const int mx = halves_max(max(ma, mb));
+    for (int r = 2; r < 16; r += 2) mb = max(max(mb, s1[r]), s1[r + 1]);
+    const int mx = halves_max(max(ma, mb)) - kScoreBias;
     const float m_new = fmaxf(m, (float)mx * sj);
     alpha = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
     const float off = kLog2Of448 - m_new;
-    vf1 = load_vfrag(vbase, 3);
     ro[2] = mfma_pv(vf0, pprev, ro[2]);
     SAGE_FENCE();
     float x[32];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = __builtin_fmaf((float)s0[r], sj, off);
+    for (int r = 0; r < 8; ++r) x[r] = __builtin_fmaf(unbias(s0[r]), sj, off);
     v4i ka = load_kfrag(kbase, 0, 0);
     v4i kb = load_kfrag(kbase, 1, 0);
     ro[3] = mfma_pv(vf1, pprev, ro[3]);
     SAGE_FENCE();
 #pragma unroll
-    for (int r = 8; r < 16; ++r) x[r] = __builtin_fmaf((float)s0[r], sj, off);
-    v16i n0 = mfma_qk(ka, qf[0], v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});
+    for (int r = 8; r < 16; ++r) x[r] = __builtin_fmaf(unbias(s0[r]), sj, off);
+    v16i n0 = mfma_qk(ka, qf[0], bias);
     ka = load_kfrag(kbase, 0, 1);
     SAGE_FENCE();
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[16 + r] = __builtin_fmaf((float)s1[r], sj, off);
-    v16i n1 = mfma_qk(kb, qf[0], v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0});
+    for (int r = 0; r < 8; ++r) x[16 + r] = __builtin_fmaf(unbias(s1[r]), sj, off);
+    v16i n1 = mfma_qk(kb, qf[0], bias);
     kb = load_kfrag(kbase, 1, 1);
     SAGE_FENCE();
 #pragma unroll
-    for (int r = 8; r < 16; ++r) x[16 + r] = __builtin_fmaf((float)s1[r], sj, off);
+    for (int r = 8; r < 16; ++r) x[16 + r] = __builtin_fmaf(unbias(s1[r]), sj, off);
     n0 = mfma_qk(ka, qf[1], n0);
     ka = load_kfrag(kbase, 0, 2);
     SAGE_FENCE();
@@ -320,6 +333,11 @@ __device__ __forceinline__ void steady_iteration(const int8_t* vtile_prev, const
         pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
     }
     n1 = mfma_qk(kb, qf[3], n1);
+    // first two V operands of the next iteration's PV (that tile is already
+    // published), so its first matrix instructions do not wait on LDS
+    const int8_t* vnext = vtile_after + lane * 16;
+    va = load_vfrag(vnext, 0);
+    vb = load_vfrag(vnext, 1);
     SAGE_FENCE();
 #pragma unroll
     for (int r = 16; r < 32; r += 4) {
@@ -384,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     v16i s0, s1;
-    if (active) qk_tile(lds_k, qf, lane, s0, s1);
+    if (active) qk_tile(lds_k, qf, lane, s0, s1, kScoreBias);
     __syncthreads();   // K slot 0 is refilled in iteration 0
 
     float m = -INFINITY;
@@ -399,6 +417,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     // alpha of the previous tile, applied to RO just before that tile's PV
     float alpha_prev = 1.0f;
     bool pending = false;
+    // kept in registers for the whole loop (the empty asm hides the constant
+    // from the compiler, which would otherwise rebuild it every iteration)
+    v16i bias = v16i{kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
+                     kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
+                     kScoreBias, kScoreBias};
+    asm volatile("" : "+v"(bias));
     // Ring slots by role, rotated each iteration: kq holds K(j+1) for this
     // iteration's QK and kf receives K(j+3); vp holds V(j-1) for this
     // iteration's PV and vf receives V(j+2).
@@ -409,19 +433,23 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     int8_t* v0 = lds_v;
     int8_t* v1 = lds_v + kTileBytes;
     int8_t* vf = lds_v + 2 * kTileBytes;
+    v8i va = load_vfrag(vp + lane * 16, 0);
+    v8i vb = load_vfrag(vp + lane * 16, 1);
+    float ksj = ksc[0];    // K scales are read one tile ahead
     for (int j = 0; j < T - 1; ++j) {
-        const float ksj = ksc[j];
+        const float ksj_next = ksc[min(j + 1, T - 1)];
         tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, wave, lane);
         tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, wave, lane);
         if (active) {
             if (pending) rescale(ro, alpha_prev);
-            steady_iteration(vp, kq, qf, lane, (qs * ksj) * c, m, dpart, alpha_prev, pprev, s0, s1, ro);
+            steady_iteration(vp, kq, v0, va, vb, qf, lane, (qs * ksj) * c, m, dpart, alpha_prev, pprev, s0, s1, ro, bias);
             pending = __any(alpha_prev != 1.0f);
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
         block_barrier();
         int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
         t = vp;  vp = v0;  v0 = v1;  v1 = vf;  vf = t;
+        ksj = ksj_next;
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
@@ -479,7 +507,7 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(DebugQkArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const v4i*)(qp + kk * 1024);
     v16i s0, s1;
-    qk_tile(kt, qf, lane, s0, s1);
+    qk_tile(kt, qf, lane, s0, s1, 0);
     const int64_t Nq = (int64_t)a.G * kQG, Nk = (int64_t)a.T * kBK;
     int32_t* out = a.s_out + ((int64_t)bh * Nq + g * kQG + (lane & 31)) * Nk + (int64_t)t * kBK;
 #pragma unroll
