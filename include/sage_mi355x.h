@@ -156,6 +156,26 @@ sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, cons
 sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale,
                                     const sage_bf16_out* o, void* stream);
 
+/* A sub-range of the attention work ("State-Ownership Architecture Decision",
+ * Interface And Future Ulysses Layout: the work descriptor carries a query
+ * row range, a head range and destination strides, while every query still
+ * walks the whole KV sequence in order).  Rows q_start .. q_start+q_count-1
+ * and heads head_start .. head_start+head_count-1 of every batch entry. */
+typedef struct sage_range {
+    int32_t q_start, q_count;
+    int32_t head_start, head_count;
+} sage_range;
+
+/* sage_attn_fwd_quantized restricted to *r: output row (b, q_start + i,
+ * head_start + j) is stored at o[b, i, j, :], so o is a [B, q_count,
+ * head_count, 128] view (it may start at any offset of a larger buffer);
+ * nothing outside those rows is written.  Each stored row is bit-identical to
+ * the same row of the full call; the work done is whole 32-row groups of the
+ * range.  Errors: as sage_attn_fwd_quantized; INVALID_ARGUMENT when r is NULL
+ * or a range is empty or leaves [0, N) x [0, H). */
+sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
+                                          const sage_bf16_out* o, void* stream);
+
 /* Whole path: carve ws, sage_quantize_qkv, then sage_attn_fwd_quantized, all
  * on `stream`.  ws must hold sage_workspace_bytes(s) bytes, 256-byte aligned.
  * Errors: as the calls above, and WORKSPACE. */

@@ -35,6 +35,11 @@ class _In(ctypes.Structure):
                 ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class _Range(ctypes.Structure):
+    _fields_ = [("q_start", ctypes.c_int32), ("q_count", ctypes.c_int32),
+                ("head_start", ctypes.c_int32), ("head_count", ctypes.c_int32)]
+
+
 class _Out(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
@@ -73,6 +78,9 @@ def _load():
     lib.sage_quantize_qkv.restype = st
     lib.sage_attn_fwd_quantized.argtypes = [ctypes.POINTER(_Quantized), ctypes.c_float, ctypes.POINTER(_Out), P]
     lib.sage_attn_fwd_quantized.restype = st
+    lib.sage_attn_fwd_quantized_range.argtypes = [ctypes.POINTER(_Quantized), ctypes.c_float,
+                                                  ctypes.POINTER(_Range), ctypes.POINTER(_Out), P]
+    lib.sage_attn_fwd_quantized_range.restype = st
     lib.sage_attn_fwd.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.c_float, ctypes.POINTER(_Out),
                                                               P, ctypes.c_size_t, P]
     lib.sage_attn_fwd.restype = st
@@ -120,11 +128,13 @@ def _in_desc(x, name):
     return _In(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
 
 
-def _out_desc(o):
+def _out_desc(o, shape):
     torch = _torch()
     if not isinstance(o, torch.Tensor) or o.device.type != "cuda" or o.dtype != torch.bfloat16 \
             or o.dim() != 4 or o.shape[3] != HEAD_DIM or o.stride(3) != 1:
         raise SageError("out must be a BF16 GPU tensor [B, N, H, 128] with unit stride along the last dimension")
+    if tuple(o.shape) != tuple(shape):
+        raise SageError("out has shape %s, expected %s" % (tuple(o.shape), tuple(shape)))
     return _Out(o.data_ptr(), o.stride(0), o.stride(1), o.stride(2))
 
 
@@ -228,9 +238,26 @@ def attn_fwd_quantized(qz: Quantized, sm_scale: float = None, out=None):
         sm_scale = default_sm_scale()
     if out is None:
         out = torch.empty((qz.B, qz.N, qz.H, HEAD_DIM), dtype=torch.bfloat16, device=qz.device)
-    do = _out_desc(out)
+    do = _out_desc(out, (qz.B, qz.N, qz.H, HEAD_DIM))
     _check(_load().sage_attn_fwd_quantized(ctypes.byref(qz.c), ctypes.c_float(sm_scale), ctypes.byref(do),
                                            _stream_ptr(out)))
+    return out
+
+
+def attn_fwd_quantized_range(qz: Quantized, q_start: int, q_count: int, head_start: int, head_count: int,
+                             sm_scale: float = None, out=None):
+    """The mainloop for query rows [q_start, q_start + q_count) and heads
+    [head_start, head_start + head_count); returns (or fills) the BF16
+    [B, q_count, head_count, 128] view of those rows."""
+    torch = _torch()
+    if sm_scale is None:
+        sm_scale = default_sm_scale()
+    if out is None:
+        out = torch.empty((qz.B, q_count, head_count, HEAD_DIM), dtype=torch.bfloat16, device=qz.device)
+    do = _out_desc(out, (qz.B, q_count, head_count, HEAD_DIM))
+    r = _Range(q_start, q_count, head_start, head_count)
+    _check(_load().sage_attn_fwd_quantized_range(ctypes.byref(qz.c), ctypes.c_float(sm_scale), ctypes.byref(r),
+                                                 ctypes.byref(do), _stream_ptr(out)))
     return out
 
 
@@ -245,7 +272,7 @@ def attn_fwd(q, k, v, sm_scale: float = None, out=None, workspace=None):
         sm_scale = default_sm_scale()
     if out is None:
         out = torch.empty((B, N, H, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
-    do = _out_desc(out)
+    do = _out_desc(out, (B, N, H, HEAD_DIM))
     if workspace is None:
         ws, off, n = _workspace(B, N, H, q.device)
     else:

@@ -361,13 +361,15 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = item / a.n_qblk;
-    const int qb = item - bh * a.n_qblk;
-    const int b = bh / a.H, h = bh - b * a.H;
+    const int bhl = item / a.n_qblk;              // (b, head within the range)
+    const int qb = item - bhl * a.n_qblk;
+    const int b = bhl / a.h_count, hl = bhl - b * a.h_count;
+    const int h = a.h_start + hl;
+    const int bh = b * a.H + h;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
-    const int g = qb * kWaves + wave;
-    const bool active = g < a.G && g * kQG < a.N;
+    const int g = a.g_begin + qb * kWaves + wave;
+    const bool active = g < a.g_end && g * kQG < a.N;
     const int T = a.T;
     const int tid16 = threadIdx.x * 16;
 
@@ -468,8 +470,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     const float dtot = halves_sum(dpart);
     const float rcp = 1.0f / dtot;
     const int n = g * kQG + (lane & 31);
-    if (n >= a.N) return;
-    uint16_t* op = a.o + b * a.o_sb + (int64_t)n * a.o_sn + h * a.o_sh;
+    if (n < a.q_start || n >= a.q_end) return;
+    uint16_t* op = a.o + b * a.o_sb + (int64_t)(n - a.q_start) * a.o_sn + hl * a.o_sh;
     const float* vs = a.v_scale + (int64_t)bh * kHD;
     const int h4 = 4 * (lane >> 5);
 #pragma unroll

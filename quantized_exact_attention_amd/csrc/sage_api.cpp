@@ -194,12 +194,19 @@ sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, cons
     return hip_status(sage::launch_prepass(p, (hipStream_t)stream), "prepass launch");
 }
 
-sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, const sage_bf16_out* o,
-                                    void* stream) {
+sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
+                                          const sage_bf16_out* o, void* stream) {
     clear_err();
     Dims d;
     sage_status st;
     if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
+    if (!r) return fail(SAGE_ERR_INVALID_ARGUMENT, "range descriptor is NULL");
+    if (r->q_start < 0 || r->q_count < 1 || (int64_t)r->q_start + r->q_count > d.N)
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "query range [%d, %d + %d) is empty or outside [0, %lld)",
+                    r->q_start, r->q_start, r->q_count, (long long)d.N);
+    if (r->head_start < 0 || r->head_count < 1 || (int64_t)r->head_start + r->head_count > d.H)
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "head range [%d, %d + %d) is empty or outside [0, %lld)",
+                    r->head_start, r->head_start, r->head_count, (long long)d.H);
     if ((st = check_out(o)) != SAGE_OK) return st;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
@@ -209,13 +216,29 @@ sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, co
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.o = (uint16_t*)o->data; p.o_sb = o->stride_b; p.o_sn = o->stride_n; p.o_sh = o->stride_h;
     p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
-    p.n_qblk = (int)((d.G + sage::kMainloopWaves - 1) / sage::kMainloopWaves);
-    const int64_t items = d.B * d.H * p.n_qblk;
+    p.q_start = r->q_start;
+    p.q_end = r->q_start + r->q_count;
+    p.h_start = r->head_start;
+    p.h_count = r->head_count;
+    p.g_begin = p.q_start / 32;
+    p.g_end = (p.q_end + 31) / 32;
+    p.n_qblk = (p.g_end - p.g_begin + sage::kMainloopWaves - 1) / sage::kMainloopWaves;
+    const int64_t items = d.B * (int64_t)r->head_count * p.n_qblk;
     if (items > 0x7fffffff) return fail(SAGE_ERR_UNSUPPORTED, "too many work items");
     p.n_items = (int)items;
     const float log2e = 1.4426950408889634f;
     p.c = sm_scale * log2e;
     return hip_status(sage::launch_mainloop(p, (hipStream_t)stream), "mainloop launch");
+}
+
+sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, const sage_bf16_out* o,
+                                    void* stream) {
+    clear_err();
+    Dims d;
+    sage_status st;
+    if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
+    const sage_range all = {0, (int32_t)d.N, 0, (int32_t)d.H};
+    return sage_attn_fwd_quantized_range(qz, sm_scale, &all, o, stream);
 }
 
 sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v, sage_shape s,

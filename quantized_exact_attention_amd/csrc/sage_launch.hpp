@@ -67,10 +67,13 @@ struct MainloopArgs {
     const int8_t* q_i8; const float* q_scale;
     const int8_t* k_i8; const float* k_scale;
     const uint8_t* v_fp8; const float* v_scale;
-    uint16_t* o; int64_t o_sb, o_sn, o_sh;
+    uint16_t* o; int64_t o_sb, o_sn, o_sh;   // output view of the range
     int B, N, H, T, G;
-    int n_qblk;          // workgroup Q blocks per (b, h)
-    int n_items;         // B * H * n_qblk
+    int q_start, q_end;  // query rows [q_start, q_end) are written
+    int h_start, h_count;
+    int g_begin, g_end;  // 32-row groups overlapping the rows
+    int n_qblk;          // workgroup Q blocks per (b, h) of the range
+    int n_items;         // B * h_count * n_qblk
     float c;             // sm_scale * log2(e), rounded to FP32
 };
 

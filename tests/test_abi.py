@@ -153,3 +153,19 @@ def test_layout_unpack_roundtrip():
     db = 3
     assert v[0, 1, 64 * t + 32 * half + 8 * (i // 4) + 4 * (l // 32) + i % 4, 32 * db + l % 32] == \
         ((1 * T + t) * 8192 + ((db * 2 + half) * 64 + l) * 16 + i)
+
+
+def test_range_validation_happens_before_launch(sage):
+    """Empty or out-of-bounds query/head ranges are rejected on the host."""
+    lib = sage._load()
+    qz = _carved(sage, N=200, H=2)
+    out = sage._Out(0x7f0000000000, 200 * 2 * 128, 2 * 128, 128)
+    bad = [(0, 0, 0, 2), (-1, 10, 0, 2), (150, 51, 0, 2), (0, 200, 0, 3), (0, 200, 2, 1), (0, 200, -1, 2),
+           (0, 200, 0, 0)]
+    for r in bad:
+        rr = sage._Range(*r)
+        assert lib.sage_attn_fwd_quantized_range(ctypes.byref(qz), ctypes.c_float(0.088), ctypes.byref(rr),
+                                                 ctypes.byref(out), None) == 1, r
+        assert b"range" in lib.sage_last_error_message()
+    assert lib.sage_attn_fwd_quantized_range(ctypes.byref(qz), ctypes.c_float(0.088), None,
+                                             ctypes.byref(out), None) == 1

@@ -263,3 +263,64 @@ def test_closed_form_v_ones_and_q_zero_on_gpu(sage):
     dec = oracle.e4m3_decode(qz.v8.ravel()).reshape(qz.v8.shape).astype(np.float64)
     mean = dec[:, :, :200].mean(axis=2) * qz.v_scale.astype(np.float64)
     assert np.max(np.abs(o - mean[:, None])) <= 2.0 ** -7 * np.abs(mean).max() + 1e-6
+
+
+@pytest.mark.parametrize("layout", ["separate", "projection"])
+def test_batched_inputs_bit_exact_bytes_and_output(sage, layout):
+    """B = 2: every batch entry's bytes, scales and output rows against the
+    oracle (batch strides are part of the input views)."""
+    import oracle
+    w = workloads.Workload("batch2_" + layout, 2, 150, 3, seed=700, layout=layout)
+    _log("batched parity: %s" % w.name)
+    inp = workloads.generate(w)
+    q, k, v = _to_gpu(inp)
+    qz = sage.quantize_qkv(q, k, v)
+    out = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(inp.q, inp.k, inp.v)
+    B, N, H = w.B, w.N, w.H
+    assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
+    assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    assert np.array_equal(layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N), ref.q_i8)
+    assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N), ref.k_i8)
+    assert np.array_equal(layouts.v_logical(qz.v_fp8.cpu().numpy(), B, H, N), ref.v8)
+    bb, hh, rr = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    rows = np.stack([bb.ravel(), hh.ravel(), rr.ravel()], axis=1)
+    ref_bits, _ = oracle.attn_rows(ref, rows)
+    got_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got = _dec_bf16(got_bits).astype(np.float64)
+    want = _dec_bf16(ref_bits).astype(np.float64)
+    assert np.max(np.abs(got - want)) <= MAX_ABS
+    assert _cos(got, want) >= MIN_COS
+
+
+@pytest.mark.parametrize("q_start,q_count,h_start,h_count",
+                         [(0, 4096, 2, 3), (37, 100, 0, 8), (4000, 96, 7, 1), (1000, 1, 3, 2), (64, 256, 0, 8)])
+def test_range_rows_equal_full_call(sage, q_start, q_count, h_start, h_count):
+    """A sub-range call writes exactly its rows and heads, at the destination
+    offset, bit-identical to the same rows of the full call."""
+    q, k, v = _to_gpu(_cpu_inputs("mid"))
+    qz = sage.quantize_qkv(q, k, v)
+    full = sage.attn_fwd_quantized(qz)
+    big = torch.full((1, q_count + 5, h_count + 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, 2:2 + q_count, 1:1 + h_count]
+    sage.attn_fwd_quantized_range(qz, q_start, q_count, h_start, h_count, out=view)
+    torch.cuda.synchronize()
+    want = full[:, q_start:q_start + q_count, h_start:h_start + h_count]
+    assert torch.equal(view.view(torch.int16), want.view(torch.int16))
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, 2:2 + q_count, 1:1 + h_count] = False
+    assert torch.all(big[mask] == 3.0)
+
+
+def test_range_one_gpu_share_of_canonical(sage):
+    """The single-GPU half of head sharding: 7 of the 56 heads over all
+    37,810 rows equal those heads of the full call."""
+    q, k, v = _to_gpu(_cpu_inputs("canonical"))
+    qz = sage.quantize_qkv(q, k, v)
+    full = sage.attn_fwd_quantized(qz)
+    part = sage.attn_fwd_quantized_range(qz, 0, q.shape[1], 14, 7)
+    torch.cuda.synchronize()
+    assert torch.equal(part.view(torch.int16), full[:, :, 14:21].view(torch.int16))
