@@ -176,9 +176,14 @@ typedef struct sage_range {
 sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
                                           const sage_bf16_out* o, void* stream);
 
-/* Whole path: carve ws, sage_quantize_qkv, then sage_attn_fwd_quantized, all
- * on `stream`.  ws must hold sage_workspace_bytes(s) bytes, 256-byte aligned.
- * Errors: as the calls above, and WORKSPACE. */
+/* Whole path in one call, all on `stream`: carve ws, the prepass for K and V,
+ * then the mainloop, which quantizes each 32-row Q group itself from the BF16
+ * view with the prepass's arithmetic (the Q producer embedded in the
+ * mainloop, "State-Ownership Architecture Decision", VEA-B: producers may be
+ * embedded to feed the slots).  The codes, scales and output are identical to
+ * sage_quantize_qkv + sage_attn_fwd_quantized; the workspace's q_i8 and
+ * q_scale regions are left unwritten.  ws must hold sage_workspace_bytes(s)
+ * bytes, 256-byte aligned.  Errors: as the calls above, and WORKSPACE. */
 sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
                           sage_shape s, float sm_scale, const sage_bf16_out* o,
                           void* ws, size_t ws_bytes, void* stream);

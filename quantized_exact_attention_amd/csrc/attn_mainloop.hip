@@ -375,7 +375,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
 
     v4i qf[4];
     float qs = 0.0f;
-    if (active) {
+    if (a.q_bf16) {
+        // The one-call path quantizes the wave's Q group here, from BF16, with
+        // the prepass's own group routine: identical codes and scale.
+        const int nq = g * kQG + (lane & 31);
+        const uint16_t* qp = a.q_bf16 + b * a.q_sb + (int64_t)nq * a.q_sn + h * a.q_sh + 16 * (lane >> 5);
+        uint4 codes[4];
+        qs = quant_q_group(qp, active && nq < a.N, codes);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[kk] = v4i{(int)codes[kk].x, (int)codes[kk].y, (int)codes[kk].z, (int)codes[kk].w};
+    } else if (active) {
         const int8_t* qp = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const v4i*)(qp + kk * 1024);

@@ -27,16 +27,6 @@ namespace sage {
 
 namespace {
 
-// 8 BF16 values (one 16-byte load) -> 8 FP32.
-__device__ __forceinline__ void unpack8(const uint4 w, float* f) {
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(u[i] << 16);
-        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
-}
-
 // 16 threads per (b, h, tile); thread c8 owns channels 8*c8 .. 8*c8+7.
 __global__ __launch_bounds__(256) void tile_stats_kernel(StatsArgs a) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -101,19 +91,6 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     a.v_inv[(int64_t)bh * kHD + d] = inv;
 }
 
-// 16 INT8 codes of x[0..15] * inv, packed little-endian into a uint4.
-__device__ __forceinline__ uint4 pack16_int8(const float* x, float inv) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc |= ((uint32_t)int8_code(x[4 * j + i], inv) & 0xffu) << (8 * i);
-        w[j] = acc;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // One wave per (b, h, 32-row group g).  Lane l reads row 32g + l%32, channels
 // 32kk + 16*(l/32) + 0..15, which is exactly the 16 bytes it writes for kk.
 __global__ __launch_bounds__(256) void quant_q_kernel(QuantQArgs a) {
@@ -124,32 +101,12 @@ __global__ __launch_bounds__(256) void quant_q_kernel(QuantQArgs a) {
     const int g = (int)(w % a.G);
     const int b = bh / a.H, h = bh % a.H;
     const int n = g * kQG + (lane & 31);
-    const bool valid = n < a.N;
     const uint16_t* qp = a.q + b * a.sb + (int64_t)n * a.sn + h * a.sh + 16 * (lane >> 5);
-    float x[64];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
-        if (valid) {
-            w0 = *(const uint4*)(qp + 32 * kk);
-            w1 = *(const uint4*)(qp + 32 * kk + 8);
-        }
-        unpack8(w0, x + 16 * kk);
-        unpack8(w1, x + 16 * kk + 8);
-    }
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) am = fmaxf(am, fabsf(x[i]));
-    am = wave_max(am);
-    float scale = 0.0f, inv = 0.0f;
-    if (am >= kAmaxFloor) {
-        scale = am / 127.0f;
-        inv = 127.0f / am;
-    }
+    uint4 codes[4];
+    const float scale = quant_q_group(qp, n < a.N, codes);
     int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        *(uint4*)(out + kk * 64 * 16) = pack16_int8(x + 16 * kk, inv);
+    for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
     if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
 }
 
@@ -298,7 +255,7 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         a.k_mean = p.k_mean; a.v_scale = p.v_scale; a.v_inv = p.v_inv;
         hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(128), 0, stream, a);
     }
-    {
+    if (p.with_q) {
         QuantQArgs a;
         a.q = p.q; a.sb = p.q_sb; a.sn = p.q_sn; a.sh = p.q_sh;
         a.H = p.H; a.N = p.N; a.G = p.G; a.waves = BH * p.G;

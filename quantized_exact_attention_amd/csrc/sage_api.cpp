@@ -115,6 +115,67 @@ sage_status hip_status(hipError_t e, const char* what) {
     return SAGE_OK;
 }
 
+sage_status prepass(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                    const sage_quantized* qz, bool with_q, void* stream) {
+    Dims d;
+    sage_status st;
+    if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
+    if ((st = check_in(q, "q")) != SAGE_OK) return st;
+    if ((st = check_in(k, "k")) != SAGE_OK) return st;
+    if ((st = check_in(v, "v")) != SAGE_OK) return st;
+    sage::PrepassArgs p;
+    p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
+    p.with_q = with_q;
+    p.q = (const uint16_t*)q->data; p.q_sb = q->stride_b; p.q_sn = q->stride_n; p.q_sh = q->stride_h;
+    p.k = (const uint16_t*)k->data; p.k_sb = k->stride_b; p.k_sn = k->stride_n; p.k_sh = k->stride_h;
+    p.v = (const uint16_t*)v->data; p.v_sb = v->stride_b; p.v_sn = v->stride_n; p.v_sh = v->stride_h;
+    p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
+    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_mean = qz->k_mean;
+    p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
+    p.k_tile_sum = qz->k_tile_sum; p.v_tile_amax = qz->v_tile_amax; p.v_inv = qz->v_inv;
+    return hip_status(sage::launch_prepass(p, (hipStream_t)stream), "prepass launch");
+}
+
+// The mainloop over range *r; q_src non-null makes it quantize Q from BF16.
+sage_status mainloop(const sage_quantized* qz, float sm_scale, const sage_range* r, const sage_bf16_out* o,
+                     const sage_bf16_in* q_src, void* stream) {
+    Dims d;
+    sage_status st;
+    if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
+    if (!r) return fail(SAGE_ERR_INVALID_ARGUMENT, "range descriptor is NULL");
+    if (r->q_start < 0 || r->q_count < 1 || (int64_t)r->q_start + r->q_count > d.N)
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "query range [%d, %d + %d) is empty or outside [0, %lld)",
+                    r->q_start, r->q_start, r->q_count, (long long)d.N);
+    if (r->head_start < 0 || r->head_count < 1 || (int64_t)r->head_start + r->head_count > d.H)
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "head range [%d, %d + %d) is empty or outside [0, %lld)",
+                    r->head_start, r->head_start, r->head_count, (long long)d.H);
+    if ((st = check_out(o)) != SAGE_OK) return st;
+    if (q_src && (st = check_in(q_src, "q")) != SAGE_OK) return st;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+    sage::MainloopArgs p;
+    p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
+    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale;
+    p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
+    p.q_bf16 = q_src ? (const uint16_t*)q_src->data : nullptr;
+    p.q_sb = q_src ? q_src->stride_b : 0; p.q_sn = q_src ? q_src->stride_n : 0; p.q_sh = q_src ? q_src->stride_h : 0;
+    p.o = (uint16_t*)o->data; p.o_sb = o->stride_b; p.o_sn = o->stride_n; p.o_sh = o->stride_h;
+    p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
+    p.q_start = r->q_start;
+    p.q_end = r->q_start + r->q_count;
+    p.h_start = r->head_start;
+    p.h_count = r->head_count;
+    p.g_begin = p.q_start / 32;
+    p.g_end = (p.q_end + 31) / 32;
+    p.n_qblk = (p.g_end - p.g_begin + sage::kMainloopWaves - 1) / sage::kMainloopWaves;
+    const int64_t items = d.B * (int64_t)r->head_count * p.n_qblk;
+    if (items > 0x7fffffff) return fail(SAGE_ERR_UNSUPPORTED, "too many work items");
+    p.n_items = (int)items;
+    const float log2e = 1.4426950408889634f;
+    p.c = sm_scale * log2e;
+    return hip_status(sage::launch_mainloop(p, (hipStream_t)stream), "mainloop launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,59 +237,13 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
 sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
                               const sage_quantized* qz, void* stream) {
     clear_err();
-    Dims d;
-    sage_status st;
-    if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
-    if ((st = check_in(q, "q")) != SAGE_OK) return st;
-    if ((st = check_in(k, "k")) != SAGE_OK) return st;
-    if ((st = check_in(v, "v")) != SAGE_OK) return st;
-    sage::PrepassArgs p;
-    p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
-    p.q = (const uint16_t*)q->data; p.q_sb = q->stride_b; p.q_sn = q->stride_n; p.q_sh = q->stride_h;
-    p.k = (const uint16_t*)k->data; p.k_sb = k->stride_b; p.k_sn = k->stride_n; p.k_sh = k->stride_h;
-    p.v = (const uint16_t*)v->data; p.v_sb = v->stride_b; p.v_sn = v->stride_n; p.v_sh = v->stride_h;
-    p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
-    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_mean = qz->k_mean;
-    p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
-    p.k_tile_sum = qz->k_tile_sum; p.v_tile_amax = qz->v_tile_amax; p.v_inv = qz->v_inv;
-    return hip_status(sage::launch_prepass(p, (hipStream_t)stream), "prepass launch");
+    return prepass(q, k, v, qz, true, stream);
 }
 
 sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
                                           const sage_bf16_out* o, void* stream) {
     clear_err();
-    Dims d;
-    sage_status st;
-    if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
-    if (!r) return fail(SAGE_ERR_INVALID_ARGUMENT, "range descriptor is NULL");
-    if (r->q_start < 0 || r->q_count < 1 || (int64_t)r->q_start + r->q_count > d.N)
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "query range [%d, %d + %d) is empty or outside [0, %lld)",
-                    r->q_start, r->q_start, r->q_count, (long long)d.N);
-    if (r->head_start < 0 || r->head_count < 1 || (int64_t)r->head_start + r->head_count > d.H)
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "head range [%d, %d + %d) is empty or outside [0, %lld)",
-                    r->head_start, r->head_start, r->head_count, (long long)d.H);
-    if ((st = check_out(o)) != SAGE_OK) return st;
-    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
-    sage::MainloopArgs p;
-    p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
-    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale;
-    p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
-    p.o = (uint16_t*)o->data; p.o_sb = o->stride_b; p.o_sn = o->stride_n; p.o_sh = o->stride_h;
-    p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
-    p.q_start = r->q_start;
-    p.q_end = r->q_start + r->q_count;
-    p.h_start = r->head_start;
-    p.h_count = r->head_count;
-    p.g_begin = p.q_start / 32;
-    p.g_end = (p.q_end + 31) / 32;
-    p.n_qblk = (p.g_end - p.g_begin + sage::kMainloopWaves - 1) / sage::kMainloopWaves;
-    const int64_t items = d.B * (int64_t)r->head_count * p.n_qblk;
-    if (items > 0x7fffffff) return fail(SAGE_ERR_UNSUPPORTED, "too many work items");
-    p.n_items = (int)items;
-    const float log2e = 1.4426950408889634f;
-    p.c = sm_scale * log2e;
-    return hip_status(sage::launch_mainloop(p, (hipStream_t)stream), "mainloop launch");
+    return mainloop(qz, sm_scale, r, o, nullptr, stream);
 }
 
 sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, const sage_bf16_out* o,
@@ -250,8 +265,11 @@ sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sa
     if ((st = check_out(o)) != SAGE_OK) return st;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
         return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
-    if ((st = sage_quantize_qkv(q, k, v, &qz, stream)) != SAGE_OK) return st;
-    return sage_attn_fwd_quantized(&qz, sm_scale, o, stream);
+    if ((st = check_in(q, "q")) != SAGE_OK) return st;
+    // K and V through the prepass; Q is quantized inside the mainloop.
+    if ((st = prepass(q, k, v, &qz, false, stream)) != SAGE_OK) return st;
+    const sage_range all = {0, s.N, 0, s.H};
+    return mainloop(&qz, sm_scale, &all, o, q, stream);
 }
 
 sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* stream) {

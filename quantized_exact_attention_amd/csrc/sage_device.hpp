@@ -49,10 +49,66 @@ __device__ __forceinline__ int int8_code(float x, float inv) {
     return (int)r;
 }
 
+// 8 BF16 values (one 16-byte load) -> 8 FP32.
+__device__ __forceinline__ void unpack8(const uint4 w, float* f) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+
+// 16 INT8 codes of x[0..15] * inv, packed little-endian into a uint4.
+__device__ __forceinline__ uint4 pack16_int8(const float* x, float inv) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc |= ((uint32_t)int8_code(x[4 * j + i], inv) & 0xffu) << (8 * i);
+        w[j] = acc;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
     return v;
+}
+
+// INT8 quantization of one 32-row Q group by one wavefront ("Sage2 Blackwell
+// Mainloop", Existing Contract: per-warp INT8 Q in 32-row groups).  Lane l
+// passes `row` = its row 32g + l%32 at channel 16*(l/32) (valid = row < N);
+// it loads channels 32kk + 16*(l/32) + 0..15 for kk = 0..3, which are exactly
+// the 16 codes it owns in the operand layout of the QK instruction.  The
+// group scale is amax/127 and each code rne(x * (127/amax)) clamped to
+// +-127; a group with amax < 2^-100 gets scale 0 and zero codes.
+__device__ __forceinline__ float quant_q_group(const uint16_t* row, bool valid, uint4 (&codes)[4]) {
+    float x[64];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
+        if (valid) {
+            w0 = *(const uint4*)(row + 32 * kk);
+            w1 = *(const uint4*)(row + 32 * kk + 8);
+        }
+        unpack8(w0, x + 16 * kk);
+        unpack8(w1, x + 16 * kk + 8);
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) am = fmaxf(am, fabsf(x[i]));
+    am = wave_max(am);
+    float scale = 0.0f, inv = 0.0f;
+    if (am >= kAmaxFloor) {
+        scale = am / 127.0f;
+        inv = 127.0f / am;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) codes[kk] = pack16_int8(x + 16 * kk, inv);
+    return scale;
 }
 
 // Maximum of the 32 int32 values of two accumulator tiles (two chains, so

@@ -51,6 +51,7 @@ struct QuantVArgs {
 
 struct PrepassArgs {
     int B, N, H, T, G;
+    bool with_q;         // false: Q is quantized by the mainloop instead
     const uint16_t* q; int64_t q_sb, q_sn, q_sh;
     const uint16_t* k; int64_t k_sb, k_sn, k_sh;
     const uint16_t* v; int64_t v_sb, v_sn, v_sh;
@@ -67,6 +68,7 @@ struct MainloopArgs {
     const int8_t* q_i8; const float* q_scale;
     const int8_t* k_i8; const float* k_scale;
     const uint8_t* v_fp8; const float* v_scale;
+    const uint16_t* q_bf16; int64_t q_sb, q_sn, q_sh;  // non-null: quantize Q from BF16 here
     uint16_t* o; int64_t o_sb, o_sn, o_sh;   // output view of the range
     int B, N, H, T, G;
     int q_start, q_end;  // query rows [q_start, q_end) are written
