@@ -178,7 +178,7 @@ constexpr int kVSlots = 4;
 // Each wave copies its 1 KiB share of an 8 KiB tile from global memory into
 // an LDS slot; lane l's 16 bytes land at the wave's base + 16*l (LDS address
 // taken from M0, which is restored afterwards; the instruction reads it at
-// issue).  Issued as inline assembly so that the compiler does not
+// issue, one wait state after the SALU write).  Issued as inline assembly so that the compiler does not
 // make every later LDS read wait for these loads: the instruction writes no
 // VGPR, and the only consumer synchronisation is the explicit vmcnt wait
 // before the block barrier that publishes the tile.
@@ -192,6 +192,7 @@ __device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, i
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
             "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
             "global_load_lds_dwordx4 %1, off\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved_m0)
