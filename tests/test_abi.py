@@ -50,6 +50,8 @@ def test_workspace_bytes(sage):
     lib = sage._load()
     assert lib.sage_workspace_bytes(sage._Shape(1, 200, 2, 64)) == 0          # D must be 128
     assert lib.sage_workspace_bytes(sage._Shape(1, (1 << 24) + 1, 1, 128)) == 0
+    assert lib.sage_workspace_bytes(sage._Shape(1, 1 << 24, 1 << 13, 128)) == 0     # grid of 2^31 tiles
+    assert lib.sage_workspace_bytes(sage._Shape(1, 1 << 24, (1 << 13) - 1, 128)) > 0
     # canonical: three quantized tensors plus scales and prepass scratch
     n = sage.workspace_bytes(1, 37810, 56)
     assert 3 * 56 * 37824 * 128 < n < 3 * 56 * 37888 * 128 + 2 * 56 * 591 * 128 * 4 + (1 << 20)
