@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="canonical")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-one-call", action="store_true",
+                    help="skip timing the one-call path (profiles of the two-call mainloop only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -212,21 +214,23 @@ def main():
 
     # The one-call path (sage_attn_fwd: K/V prepass, then the mainloop that
     # quantizes Q itself), timed as whole steps on its own workspace.
-    ws, off, nbytes = sage._workspace(w.B, w.N, w.H, dev)
-    wsv = ws[off:off + nbytes]
-    out1 = torch.empty_like(out)
-    for _ in range(args.warmup):
-        sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
-    torch.cuda.synchronize(dev)
-    o_start = torch.cuda.Event(enable_timing=True)
-    o_end = torch.cuda.Event(enable_timing=True)
-    o_start.record(stream)
-    for _ in range(args.steps):
-        sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
-    o_end.record(stream)
-    torch.cuda.synchronize(dev)
-    one_call_ms = o_start.elapsed_time(o_end) / args.steps
-    log("bench: one-call step %.3f ms" % one_call_ms)
+    one_call_ms = None
+    if not args.no_one_call:
+        ws, off, nbytes = sage._workspace(w.B, w.N, w.H, dev)
+        wsv = ws[off:off + nbytes]
+        out1 = torch.empty_like(out)
+        for _ in range(args.warmup):
+            sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
+        torch.cuda.synchronize(dev)
+        o_start = torch.cuda.Event(enable_timing=True)
+        o_end = torch.cuda.Event(enable_timing=True)
+        o_start.record(stream)
+        for _ in range(args.steps):
+            sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
+        o_end.record(stream)
+        torch.cuda.synchronize(dev)
+        one_call_ms = o_start.elapsed_time(o_end) / args.steps
+        log("bench: one-call step %.3f ms" % one_call_ms)
     result = {
         "metric": METRIC,
         "value": ops / (ms_per_step * 1e-3) / 1e12,
@@ -251,7 +255,7 @@ def main():
         "mainloop_tops": achieved,
         "prepass_ms": prep_avg,
         "one_call_ms_per_step": one_call_ms,
-        "one_call_tops": ops / (one_call_ms * 1e-3) / 1e12,
+        "one_call_tops": ops / (one_call_ms * 1e-3) / 1e12 if one_call_ms else None,
         "prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (prep_avg * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
