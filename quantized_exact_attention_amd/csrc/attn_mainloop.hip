@@ -100,11 +100,11 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
 // Online softmax of one tile for this lane's query row (32 of the tile's keys
 // here, the other 32 on lane l^32), on biased sums (kScoreBias): max update on
 // the exact int32 sums (the score scale sj is positive, so the largest sum
-// gives the largest score),
-// alpha = 2^(m - m_new), p = 448 * 2^(t - m_new) with 448 folded into the
-// exponent offset, this lane's part of the denominator, and the FP8 codes
-// packed in the B-operand order of the PV instruction.  kLast masks keys at
-// or beyond `tail` in the final, partial tile.
+// gives the largest score), alpha = 2^(m - m_new), p = 448 * 2^(t - m_new)
+// with 448 folded into the exponent offset, this lane's part of the
+// denominator, and the FP8 codes packed in the B-operand order of the PV
+// instruction.  kLast masks keys at or beyond `tail` in the final, partial
+// tile.
 template <bool kLast>
 __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int tail, int lane, float& m,
                                              float& dpart, float& alpha, v8i& pk) {
@@ -166,20 +166,22 @@ __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
 
 // LDS rings: K tiles in 3 slots, V tiles in 4 slots, filled straight from
 // global memory by global_load_lds_dwordx4 (no VGPR staging).  In iteration j
-// a wave issues PV of tile j-1 (V slot (j-1)%4), the softmax of tile j
-// (scores computed in the previous iteration) and QK of tile j+1 (K slot
-// (j+1)%3), while the block's loads of K(j+3) and V(j+2) are in flight; the
-// loads issued one iteration earlier are waited for before the barrier that
-// ends the iteration.  RO receives every tile's PV in increasing tile order,
-// each after the rescale by that tile's alpha.
+// a wave issues PV of tile j-1, the softmax of tile j (scores computed in the
+// previous iteration) and QK of tile j+1, while the workgroup's loads of
+// K(j+3) and V(j+2) are in flight; the loads issued one iteration earlier are
+// waited for before the barrier that ends the iteration.  The slots change
+// roles by pointer rotation, not by index arithmetic.  RO receives every
+// tile's PV in increasing tile order, each after the rescale by that tile's
+// alpha.
 constexpr int kKSlots = 3;
 constexpr int kVSlots = 4;
 
-// Each wave copies its 1 KiB share of an 8 KiB tile from global memory into
-// an LDS slot; lane l's 16 bytes land at the wave's base + 16*l (LDS address
-// taken from M0, which is restored afterwards; the instruction reads it at
-// issue, one wait state after the SALU write).  Issued as inline assembly so that the compiler does not
-// make every later LDS read wait for these loads: the instruction writes no
+// Each wave copies its share (kTileLoads KiB) of an 8 KiB tile from global
+// memory into an LDS slot; lane l's 16 bytes of each KiB land at that KiB's
+// base + 16*l (LDS address taken from M0, which is restored afterwards; the
+// instruction reads it at issue, one wait state after the SALU write).
+// Issued as inline assembly so that the compiler does not make every later
+// LDS read wait for these loads: the instruction writes no
 // VGPR, and the only consumer synchronisation is the explicit vmcnt wait
 // before the block barrier that publishes the tile.
 __device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, int wave, int lane) {
@@ -202,8 +204,9 @@ __device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, i
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8): wait until at most 2 / 0 vector-memory
-// operations of this wave are outstanding, without waiting on the others.
+// expcnt 6:4, lgkmcnt 11:8, the other counters left at their maxima): wait
+// until no vector-memory operation of this wave is outstanding, or until at
+// most the 2 * kTileLoads tile loads issued in the current iteration are.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVmIter = 0x0F70 | (2 * kTileLoads);
 static_assert(2 * kTileLoads < 16, "vmcnt field");
