@@ -191,8 +191,10 @@ def test_attention_parity_sampled_rows(sage, name, per_head):
     _attn_check(sage, name, rows=_sample_rows(w, per_head, seed=7))
 
 
-@pytest.mark.parametrize("sm_scale", [0.02, 0.3])
+@pytest.mark.parametrize("sm_scale", [0.02, 0.3, 3.0])
 def test_attention_parity_other_scales(sage, sm_scale):
+    """Score scales from well below to well above the canonical one (3.0 makes
+    the softmax nearly one-hot)."""
     _attn_check(sage, "sweep_n129", sm_scale=sm_scale)
 
 
