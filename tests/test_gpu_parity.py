@@ -22,6 +22,12 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-2
 MIN_COS = 0.9999
+# Stronger than the tolerance: the kernel follows the oracle's arithmetic step
+# by step, so nearly every BF16 output is bit-identical; the rest differ where
+# the hardware exp2 or the matrix unit's summation order moves a probability
+# across an E4M3 rounding midpoint.  (Measured: 97.7-99.7% on every workload;
+# an approximation of the per-score arithmetic drops this to about 70%.)
+MIN_BIT_EQUAL = 0.95
 
 
 def _log(msg):
@@ -177,6 +183,7 @@ def _attn_check(sage, name, rows=None, sm_scale=None):
     _log("attn %s: rows=%d max_abs=%.3g cos=%.7f bit-equal=%.3f" % (name, len(rows), max_abs, cos, exact))
     assert max_abs <= MAX_ABS, max_abs
     assert cos >= MIN_COS, cos
+    assert exact >= MIN_BIT_EQUAL, exact
     return out
 
 
