@@ -333,3 +333,52 @@ def test_range_one_gpu_share_of_canonical(sage):
     part = sage.attn_fwd_quantized_range(qz, 0, q.shape[1], 14, 7)
     torch.cuda.synchronize()
     assert torch.equal(part.view(torch.int16), full[:, :, 14:21].view(torch.int16))
+
+
+def test_degenerate_operands_zero_scales(sage):
+    """K constant over tokens (K - mean = 0: every K scale 0, all scores 0)
+    and one all-zero V channel (scale 0): bytes and scales bit-exact, output
+    = the mean of dequantized V, and exactly 0 in the zero channel."""
+    import oracle
+    w = workloads.Workload("degenerate", 1, 300, 2, seed=900)
+    inp = workloads.generate(w)
+    k = inp.k.clone()
+    k[:] = k[:, :1]                                  # every token equals token 0
+    v = inp.v.clone()
+    v[..., 5] = 0.0
+    q, kk, vv = inp.q.cuda(), k.cuda(), v.cuda()
+    qz = sage.quantize_qkv(q, kk, vv)
+    out = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(inp.q, k, v)
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert not np.any(ref.k_scale)
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), 1, 2, 300), ref.k_i8)
+    assert np.array_equal(layouts.v_logical(qz.v_fp8.cpu().numpy(), 1, 2, 300), ref.v8)
+    o = out.float().cpu().numpy()
+    assert np.all(o[..., 5] == 0.0)
+    dec = oracle.e4m3_decode(ref.v8.ravel()).reshape(ref.v8.shape).astype(np.float64)
+    mean = dec[:, :, :300].mean(axis=2) * ref.v_scale.astype(np.float64)      # [B, H, 128]
+    assert np.max(np.abs(o - mean[:, None])) <= 2.0 ** -7 * np.abs(mean).max() + 1e-6
+
+
+def test_ragged_shape_batch3_sampled_rows(sage):
+    """B = 3, H = 5, N = 4099 (65 tiles, the last with 3 keys; 33 Q blocks):
+    sampled rows of every (batch, head) against the oracle."""
+    import oracle
+    w = workloads.Workload("ragged", 3, 4099, 5, seed=901, layout="projection")
+    _log("ragged parity: %s" % w.name)
+    inp = workloads.generate(w)
+    q, k, v = _to_gpu(inp)
+    out = sage.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(inp.q, inp.k, inp.v)
+    rows = _sample_rows(w, 24, seed=11)
+    ref_bits, _ = oracle.attn_rows(ref, rows)
+    got_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got = _dec_bf16(got_bits).astype(np.float64)
+    want = _dec_bf16(ref_bits).astype(np.float64)
+    assert np.max(np.abs(got - want)) <= MAX_ABS
+    assert _cos(got, want) >= MIN_COS
+    assert np.mean(got_bits == ref_bits) >= MIN_BIT_EQUAL
