@@ -139,11 +139,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="canonical")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="input / quantized-operand sets the steps cycle through (cold caches)")
     ap.add_argument("--no-one-call", action="store_true",
                     help="skip timing the one-call path (profiles of the two-call mainloop only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
+    if args.rotate < 1 or args.steps < 1 or args.warmup < 0:
+        ap.error("--rotate and --steps must be >= 1, --warmup >= 0")
     if args.gpus != 1:
         print("bench.py measures one GPU only (run with --gpus 1): the path is built and timed on a single "
               "MI355X; across GPUs it would shard by head, which needs no exchange when each GPU holds its "
@@ -162,12 +166,24 @@ def main():
     inp = workloads.generate(w)
     if inp.buffer is not None:
         buf = inp.buffer.to(dev)
-        q, k, v = [buf[:, :, i * w.H * HD:(i + 1) * w.H * HD].view(w.B, w.N, w.H, HD) for i in range(3)]
+        qkv = [tuple(buf[:, :, i * w.H * HD:(i + 1) * w.H * HD].view(w.B, w.N, w.H, HD) for i in range(3))]
     else:
-        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        buf = None
+        qkv = [(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev))]
     del inp
+    # Steps rotate over several copies of the inputs and of the quantized
+    # operands (each set larger than the 256 MB Infinity Cache), so no call
+    # finds its operands cached by the previous one.
+    for _ in range(args.rotate - 1):
+        if buf is not None:
+            b2 = buf.clone()
+            qkv.append(tuple(b2[:, :, i * w.H * HD:(i + 1) * w.H * HD].view(w.B, w.N, w.H, HD) for i in range(3)))
+        else:
+            qkv.append(tuple(x.clone() for x in qkv[0]))
+    q, k, v = qkv[0]
     out = torch.empty((w.B, w.N, w.H, HD), dtype=torch.bfloat16, device=dev)
-    qz = sage.Quantized(w.B, w.N, w.H, dev)
+    qzs = [sage.Quantized(w.B, w.N, w.H, dev) for _ in range(args.rotate)]
+    qz = qzs[0]
     stream = torch.cuda.current_stream(dev)
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -179,9 +195,10 @@ def main():
         del src, dst
 
     # warmup: the same calls as the timed steps
-    for _ in range(args.warmup):
-        sage.quantize_qkv(q, k, v, into=qz)
-        sage.attn_fwd_quantized(qz, out=out)
+    for i in range(args.warmup):
+        q, k, v = qkv[i % args.rotate]
+        sage.quantize_qkv(q, k, v, into=qzs[i % args.rotate])
+        sage.attn_fwd_quantized(qzs[i % args.rotate], out=out)
     torch.cuda.synchronize(dev)
     log("bench: warmup done (%d steps)" % args.warmup)
 
@@ -191,6 +208,8 @@ def main():
     torch.cuda.synchronize(dev)
     t_start.record(stream)
     for i in range(args.steps):
+        q, k, v = qkv[i % args.rotate]
+        qz = qzs[i % args.rotate]
         ev[i][0].record(stream)
         sage.quantize_qkv(q, k, v, into=qz)
         ev[i][1].record(stream)
@@ -219,13 +238,15 @@ def main():
         ws, off, nbytes = sage._workspace(w.B, w.N, w.H, dev)
         wsv = ws[off:off + nbytes]
         out1 = torch.empty_like(out)
-        for _ in range(args.warmup):
+        for i in range(args.warmup):
+            q, k, v = qkv[i % args.rotate]
             sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
         torch.cuda.synchronize(dev)
         o_start = torch.cuda.Event(enable_timing=True)
         o_end = torch.cuda.Event(enable_timing=True)
         o_start.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            q, k, v = qkv[i % args.rotate]
             sage.attn_fwd(q, k, v, out=out1, workspace=wsv)
         o_end.record(stream)
         torch.cuda.synchronize(dev)
@@ -247,6 +268,7 @@ def main():
         "config": {"workload": "%s: B=%d N=%d H=%d D=128, non-causal, %s BF16 NHD inputs, contiguous BF16 NHD output"
                                % (w.name, w.B, w.N, w.H, "projection-strided" if w.layout == "projection"
                                   else "contiguous"),
+                   "input_sets": args.rotate,
                    "global_batch": w.B, "seq_len": w.N, "heads": w.H, "head_dim": HD, "parallelism": "single GPU"},
         "mainloop_ms": main_avg,
         "mainloop_ms_p50": p50,
