@@ -55,7 +55,7 @@ typedef enum sage_status {
 } sage_status;
 
 /* Problem shape.  D must be 128; 1 <= B, H; 1 <= N <= 2^24; B*H <= 2^24 and
- * B*H*ceil(N/64) < 2^31 (launch grid limit). */
+ * B*H*2*ceil(N/128) < 2^31 (launch grid limit). */
 typedef struct sage_shape {
     int32_t B, N, H, D;
 } sage_shape;

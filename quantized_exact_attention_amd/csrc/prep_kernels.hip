@@ -16,10 +16,10 @@
 //                    channel absolute maxima of V          (reads K, V)
 //   2. finalize      per (b,h): k_mean from the tile sums in tile order; V
 //                    channel amax, v_scale = a/448, v_inv = 448/a
-//   3. quant_q       per 32-row group: amax, scale, INT8 codes (reads Q)
-//   4. quant_k       per 64-row tile: K - k_mean, amax, scale, codes (reads K)
-//   5. quant_v       per 64-row tile: E4M3 codes in the mainloop's V layout
-//                    (reads V)
+//   3. quant_qkv     per 64-row tile, one pass over its Q, K and V rows:
+//                    INT8 Q per 32-row group, INT8 K - k_mean per tile,
+//                    E4M3 V in the mainloop's layout (Q is skipped when the
+//                    mainloop quantizes it itself)
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -68,14 +68,16 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     const int d = threadIdx.x;
     const float* ks = a.k_tile_sum + (int64_t)bh * a.T * kHD + d;
     const float* va = a.v_tile_amax + (int64_t)bh * a.T * kHD + d;
+    // Sequential in tile order; loads are issued 32 tiles ahead of the adds.
+    constexpr int kBatch = 32;
     float total = 0.0f, amax = 0.0f;
     int t = 0;
-    for (; t + 8 <= a.T; t += 8) {
-        float s[8], m[8];
+    for (; t + kBatch <= a.T; t += kBatch) {
+        float s[kBatch], m[kBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { s[i] = ks[(int64_t)(t + i) * kHD]; m[i] = va[(int64_t)(t + i) * kHD]; }
+        for (int i = 0; i < kBatch; ++i) { s[i] = ks[(int64_t)(t + i) * kHD]; m[i] = va[(int64_t)(t + i) * kHD]; }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { total = total + s[i]; amax = fmaxf(amax, m[i]); }
+        for (int i = 0; i < kBatch; ++i) { total = total + s[i]; amax = fmaxf(amax, m[i]); }
     }
     for (; t < a.T; ++t) {
         total = total + ks[(int64_t)t * kHD];
@@ -91,128 +93,130 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     a.v_inv[(int64_t)bh * kHD + d] = inv;
 }
 
-// One wave per (b, h, 32-row group g).  Lane l reads row 32g + l%32, channels
-// 32kk + 16*(l/32) + 0..15, which is exactly the 16 bytes it writes for kk.
-__global__ __launch_bounds__(256) void quant_q_kernel(QuantQArgs a) {
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= a.waves) return;
-    const int lane = threadIdx.x & 63;
-    const int bh = (int)(w / a.G);
-    const int g = (int)(w % a.G);
-    const int b = bh / a.H, h = bh % a.H;
-    const int n = g * kQG + (lane & 31);
-    const uint16_t* qp = a.q + b * a.sb + (int64_t)n * a.sn + h * a.sh + 16 * (lane >> 5);
-    uint4 codes[4];
-    const float scale = quant_q_group(qp, n < a.N, codes);
-    int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
-    if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
-}
-
-// One wave per (b, h, 64-row tile t).  Lane l handles rows 64t + 32*half + l%32
-// and channels 32kk + 16*(l/32) + 0..15 for half in 0..1, kk in 0..3.
-__global__ __launch_bounds__(256) void quant_k_kernel(QuantKArgs a) {
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= a.waves) return;
-    const int lane = threadIdx.x & 63;
-    const int bh = (int)(w / a.T);
-    const int t = (int)(w % a.T);
-    const int b = bh / a.H, h = bh % a.H;
-    const int c0 = 16 * (lane >> 5);
-    const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;
-    uint4 raw[2][4][2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int n = t * kBK + 32 * half + (lane & 31);
-        const bool valid = n < a.N;
-        const uint16_t* kp = a.k + b * a.sb + (int64_t)n * a.sn + h * a.sh + c0;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            raw[half][kk][0] = valid ? *(const uint4*)(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
-            raw[half][kk][1] = valid ? *(const uint4*)(kp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
-        }
-    }
-    float am = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        float km[16];
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
-            km[i] = m4[0]; km[i + 1] = m4[1]; km[i + 2] = m4[2]; km[i + 3] = m4[3];
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int n = t * kBK + 32 * half + (lane & 31);
-            if (n < a.N) {
-                float x[16];
-                unpack8(raw[half][kk][0], x);
-                unpack8(raw[half][kk][1], x + 8);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i] - km[i]));
-            }
-        }
-    }
-    am = wave_max(am);
-    float scale = 0.0f, inv = 0.0f;
-    if (am >= kAmaxFloor) {
-        scale = am / 127.0f;
-        inv = 127.0f / am;
-    }
-    int8_t* out = a.k_i8 + ((int64_t)bh * a.T + t) * kTileBytes + lane * 16;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        float km[16];
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
-            km[i] = m4[0]; km[i + 1] = m4[1]; km[i + 2] = m4[2]; km[i + 3] = m4[3];
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int n = t * kBK + 32 * half + (lane & 31);
-            float x[16];
-            unpack8(raw[half][kk][0], x);
-            unpack8(raw[half][kk][1], x + 8);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = x[i] - km[i];
-            uint4 codes = pack16_int8(x, inv);
-            if (n >= a.N) codes = make_uint4(0, 0, 0, 0);
-            *(uint4*)(out + (half * 4 + kk) * 64 * 16) = codes;
-        }
-    }
-    if (lane == 0) a.k_scale[(int64_t)bh * a.T + t] = scale;
-}
-
-// One block of 256 threads per (b, h, 64-row tile t).  The BF16 tile is staged
-// in LDS row-major; each output chunk gathers 16 rows of one channel.
+// One block of 256 threads per (b, h, 64-row tile t) quantizes everything the
+// tile's rows hold, so each projection row segment is read once:
+//   waves 0, 1  Q groups 2t and 2t+1 (when Q is quantized here): lane l reads
+//               row 32g + l%32, channels 32kk + 16*(l/32) + 0..15, exactly the
+//               16 bytes it writes for kk
+//   waves 2, 3  K rows 64t + 32*(w-2) + l%32, same channel split; the tile's
+//               absolute maximum of K - k_mean is combined through LDS, then
+//               each wave writes the codes of its 32 rows
+//   all waves   the BF16 V tile is staged row-major in LDS; each 16-byte
+//               output chunk then gathers 16 rows of one channel in the PV
+//               operand order
+// Blocks past the last K/V tile (t >= T, only when Q is quantized: the Q
+// padding reaches 64*Tq >= 64*T rows) write the all-padding Q groups.
 constexpr int kVRow = kHD + 8;   // LDS row pitch in BF16 elements (272 bytes)
 
-__global__ __launch_bounds__(256) void quant_v_kernel(QuantVArgs a) {
+__global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
     __shared__ uint16_t tile[kBK * kVRow];
+    __shared__ float k_amax[2];
     const int64_t blk = blockIdx.x;
-    const int bh = (int)(blk / a.T);
-    const int t = (int)(blk % a.T);
+    const int bh = (int)(blk / a.Tq);
+    const int t = (int)(blk % a.Tq);
     const int b = bh / a.H, h = bh % a.H;
-    {
-        const int row = threadIdx.x >> 2;
-        const int seg = threadIdx.x & 3;                 // 32 channels each
-        const int n = t * kBK + row;
-        const uint16_t* vp = a.v + b * a.sb + (int64_t)n * a.sn + h * a.sh + 32 * seg;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const bool kv = t < a.T;   // uniform over the block
+
+    // V rows: thread (row, seg) loads 32 channels of one row.
+    const int vrow = threadIdx.x >> 2;
+    const int vseg = threadIdx.x & 3;
+    uint4 vraw[4];
+    if (kv) {
+        const int n = t * kBK + vrow;
+        const uint16_t* vp = a.v + b * a.v_sb + (int64_t)n * a.v_sn + h * a.v_sh + 32 * vseg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 w = n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
-            *(uint4*)(&tile[row * kVRow + 32 * seg + 8 * i]) = w;
+        for (int i = 0; i < 4; ++i) vraw[i] = n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
+    }
+
+    const int half = wave - 2;
+    const int c0 = 16 * (lane >> 5);
+    const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;
+    const int kn = t * kBK + 32 * half + (lane & 31);
+    uint4 kraw[4][2];
+    if (wave < 2) {
+        if (a.q != nullptr) {
+            const int g = 2 * t + wave;
+            const int n = g * kQG + (lane & 31);
+            const uint16_t* qp = a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + c0;
+            uint4 codes[4];
+            const float scale = quant_q_group(qp, n < a.N, codes);
+            int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
+            if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
         }
+    } else if (kv) {
+        // this wave's share of the tile's absolute maximum of K - k_mean
+        const bool valid = kn < a.N;
+        const uint16_t* kp = a.k + b * a.k_sb + (int64_t)kn * a.k_sn + h * a.k_sh + c0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kraw[kk][0] = valid ? *(const uint4*)(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
+            kraw[kk][1] = valid ? *(const uint4*)(kp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+        }
+        float am = 0.0f;
+        if (valid) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                float x[16];
+                unpack8(kraw[kk][0], x);
+                unpack8(kraw[kk][1], x + 8);
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    const v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
+                    am = fmaxf(am, fabsf(x[i] - m4[0]));
+                    am = fmaxf(am, fabsf(x[i + 1] - m4[1]));
+                    am = fmaxf(am, fabsf(x[i + 2] - m4[2]));
+                    am = fmaxf(am, fabsf(x[i + 3] - m4[3]));
+                }
+            }
+        }
+        am = wave_max(am);
+        if (lane == 0) k_amax[half] = am;
+    }
+    if (kv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(uint4*)(&tile[vrow * kVRow + 32 * vseg + 8 * i]) = vraw[i];
     }
     __syncthreads();
+    if (!kv) return;
+
+    if (wave >= 2) {
+        const float am = fmaxf(k_amax[0], k_amax[1]);
+        float scale = 0.0f, inv = 0.0f;
+        if (am >= kAmaxFloor) {
+            scale = am / 127.0f;
+            inv = 127.0f / am;
+        }
+        int8_t* out = a.k_i8 + ((int64_t)bh * a.T + t) * kTileBytes + lane * 16;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float x[16];
+            unpack8(kraw[kk][0], x);
+            unpack8(kraw[kk][1], x + 8);
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
+                x[i] = x[i] - m4[0];
+                x[i + 1] = x[i + 1] - m4[1];
+                x[i + 2] = x[i + 2] - m4[2];
+                x[i + 3] = x[i + 3] - m4[3];
+            }
+            uint4 codes = pack16_int8(x, inv);
+            if (kn >= a.N) codes = make_uint4(0, 0, 0, 0);
+            *(uint4*)(out + (half * 4 + kk) * 64 * 16) = codes;
+        }
+        if (wave == 2 && lane == 0) a.k_scale[(int64_t)bh * a.T + t] = scale;
+    }
+
     uint8_t* out = a.v_fp8 + ((int64_t)bh * a.T + t) * kTileBytes;
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
         const int c = threadIdx.x + 256 * rep;          // 16-byte chunk index
         const int db = c >> 7;
-        const int half = (c >> 6) & 1;
+        const int vhalf = (c >> 6) & 1;
         const int l = c & 63;
         const int d = 32 * db + (l & 31);
         const int hh = l >> 5;
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(QuantVArgs a) {
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = 32 * half + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const int key = 32 * vhalf + 8 * (i >> 2) + 4 * hh + (i & 3);
             x[i] = bf16_bits_to_f32(tile[key * kVRow + d]) * inv;
         }
         uint32_t wd[4];
@@ -255,26 +259,16 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         a.k_mean = p.k_mean; a.v_scale = p.v_scale; a.v_inv = p.v_inv;
         hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(128), 0, stream, a);
     }
-    if (p.with_q) {
-        QuantQArgs a;
-        a.q = p.q; a.sb = p.q_sb; a.sn = p.q_sn; a.sh = p.q_sh;
-        a.H = p.H; a.N = p.N; a.G = p.G; a.waves = BH * p.G;
-        a.q_i8 = p.q_i8; a.q_scale = p.q_scale;
-        hipLaunchKernelGGL(quant_q_kernel, dim3((unsigned)((a.waves + 3) / 4)), dim3(256), 0, stream, a);
-    }
     {
-        QuantKArgs a;
-        a.k = p.k; a.sb = p.k_sb; a.sn = p.k_sn; a.sh = p.k_sh;
-        a.H = p.H; a.N = p.N; a.T = p.T; a.waves = BH * p.T;
-        a.k_mean = p.k_mean; a.k_i8 = p.k_i8; a.k_scale = p.k_scale;
-        hipLaunchKernelGGL(quant_k_kernel, dim3((unsigned)((a.waves + 3) / 4)), dim3(256), 0, stream, a);
-    }
-    {
-        QuantVArgs a;
-        a.v = p.v; a.sb = p.v_sb; a.sn = p.v_sn; a.sh = p.v_sh;
-        a.H = p.H; a.N = p.N; a.T = p.T;
-        a.v_inv = p.v_inv; a.v_scale = p.v_scale; a.v_fp8 = p.v_fp8;
-        hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(BH * p.T)), dim3(256), 0, stream, a);
+        QuantArgs a;
+        a.q = p.with_q ? p.q : nullptr; a.q_sb = p.q_sb; a.q_sn = p.q_sn; a.q_sh = p.q_sh;
+        a.k = p.k; a.k_sb = p.k_sb; a.k_sn = p.k_sn; a.k_sh = p.k_sh;
+        a.v = p.v; a.v_sb = p.v_sb; a.v_sn = p.v_sn; a.v_sh = p.v_sh;
+        a.H = p.H; a.N = p.N; a.T = p.T; a.G = p.G;
+        a.Tq = p.with_q ? p.G / 2 : p.T;
+        a.k_mean = p.k_mean; a.v_inv = p.v_inv; a.v_scale = p.v_scale;
+        a.q_i8 = p.q_i8; a.q_scale = p.q_scale; a.k_i8 = p.k_i8; a.k_scale = p.k_scale; a.v_fp8 = p.v_fp8;
+        hipLaunchKernelGGL(quant_qkv_kernel, dim3((unsigned)(BH * a.Tq)), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

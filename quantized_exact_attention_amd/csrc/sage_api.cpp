@@ -44,9 +44,9 @@ bool dims_of(const sage_shape& s, Dims* d) {
     d->Nq = (s.N + 127) / 128 * 128;
     d->G = d->Nq / 32;
     d->Nk = d->T * 64;
-    // every launch grid (one block per (b, h, tile) in the V quantizer is the
-    // largest) must fit the 32-bit grid size
-    if (d->B * d->H * d->T > 0x7fffffff) return false;
+    // every launch grid must fit the 32-bit grid size; the largest is the
+    // quantizer's, one block per (b, h, 64 rows of the padded Q length)
+    if (d->B * d->H * (d->Nq / 64) > 0x7fffffff) return false;
     return true;
 }
 
@@ -99,7 +99,7 @@ sage_status check_out(const sage_bf16_out* o) {
 sage_status check_quantized(const sage_quantized* qz, Dims* d) {
     if (!qz) return fail(SAGE_ERR_INVALID_ARGUMENT, "quantized descriptor is NULL");
     if (!dims_of(qz->shape, d))
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*ceil(N/64)<2^31)",
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*2*ceil(N/128)<2^31)",
                     qz->shape.B, qz->shape.N, qz->shape.H, qz->shape.D);
     if (!qz->q_i8 || !qz->q_scale || !qz->k_i8 || !qz->k_scale || !qz->k_mean || !qz->v_fp8 || !qz->v_scale ||
         !qz->k_tile_sum || !qz->v_tile_amax || !qz->v_inv)
@@ -209,7 +209,7 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
     Dims d;
     if (!out) return fail(SAGE_ERR_INVALID_ARGUMENT, "out is NULL");
     if (!dims_of(s, &d))
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*ceil(N/64)<2^31)",
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*2*ceil(N/128)<2^31)",
                     s.B, s.N, s.H, s.D);
     if (!ws) return fail(SAGE_ERR_WORKSPACE, "workspace is NULL");
     if ((uintptr_t)ws % kAlign) return fail(SAGE_ERR_WORKSPACE, "workspace must be 256-byte aligned");

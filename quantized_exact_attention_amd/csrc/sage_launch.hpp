@@ -24,28 +24,17 @@ struct FinalizeArgs {
     float* v_inv;
 };
 
-struct QuantQArgs {
-    const uint16_t* q; int64_t sb, sn, sh;
-    int H, N, G;
-    int64_t waves;
-    int8_t* q_i8;
-    float* q_scale;
-};
-
-struct QuantKArgs {
-    const uint16_t* k; int64_t sb, sn, sh;
-    int H, N, T;
-    int64_t waves;
+struct QuantArgs {
+    const uint16_t* q; int64_t q_sb, q_sn, q_sh;   // null: Q is not quantized here
+    const uint16_t* k; int64_t k_sb, k_sn, k_sh;
+    const uint16_t* v; int64_t v_sb, v_sn, v_sh;
+    int H, N, T, G;
+    int Tq;              // 64-row tiles per (b, h) this launch covers (>= T)
     const float* k_mean;
-    int8_t* k_i8;
-    float* k_scale;
-};
-
-struct QuantVArgs {
-    const uint16_t* v; int64_t sb, sn, sh;
-    int H, N, T;
     const float* v_inv;
     const float* v_scale;
+    int8_t* q_i8; float* q_scale;
+    int8_t* k_i8; float* k_scale;
     uint8_t* v_fp8;
 };
 
