@@ -39,12 +39,13 @@ def _configure(lib):
     lib.oracle_quant_k.argtypes = [P, I64, I64, I64, I, I, I, P, P, P]
     lib.oracle_quant_q.argtypes = [P, I64, I64, I64, I, I, I, P, P]
     lib.oracle_quant_v.argtypes = [P, I64, I64, I64, I, I, I, P, P]
+    lib.oracle_norm_rope.argtypes = [P, I64, I64, I64, I, I, I, P, P, P, ctypes.c_float, P]
     lib.oracle_qk_s32.argtypes = [P, P, I, I, I, I64, I64, P]
     lib.oracle_attn_rows.argtypes = [P, P, P, P, P, P, I, I, I, ctypes.c_float, P, I64, P, P]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_e4m3_encode_n.argtypes = [P, P, I64]
     lib.oracle_f32_to_bf16_n.argtypes = [P, P, I64]
-    for name in ("oracle_k_mean", "oracle_quant_k", "oracle_quant_q", "oracle_quant_v",
+    for name in ("oracle_norm_rope", "oracle_k_mean", "oracle_quant_k", "oracle_quant_q", "oracle_quant_v",
                  "oracle_qk_s32", "oracle_attn_rows", "oracle_e4m3_encode_n",
                  "oracle_f32_to_bf16_n"):
         getattr(lib, name).restype = None
@@ -174,6 +175,26 @@ def quantize(Q, K, V) -> Quantized:
     k_i8, k_scale = quant_k(K, km)
     v8, v_scale = quant_v(V)
     return Quantized(vq.B, vq.N, vq.H, km, q_i8, q_scale, k_i8, k_scale, v8, v_scale)
+
+
+def norm_rope(X, weight, cos, sin, eps: float) -> np.ndarray:
+    """Step 0: per-head RMSNorm (FP32 weight [128]) then split-half RoPE with the
+    FP32 angle tables cos, sin [N, 64]; returns BF16 bits [B, N, H, 128]."""
+    v = _View(X)
+    g = np.ascontiguousarray(np.asarray(weight, np.float32).reshape(HD))
+    c = np.ascontiguousarray(np.asarray(cos, np.float32))
+    s = np.ascontiguousarray(np.asarray(sin, np.float32))
+    if c.shape != (v.N, HD // 2) or s.shape != (v.N, HD // 2):
+        raise ValueError("angle tables must be [N, 64]")
+    out = np.zeros((v.B, v.N, v.H, HD), np.uint16)
+    _load().oracle_norm_rope(v.ptr, *v.strides, v.B, v.N, v.H, _ptr(g), _ptr(c), _ptr(s),
+                             ctypes.c_float(eps), _ptr(out))
+    return out
+
+
+def quantize_norm_rope(Q, K, V, q_weight, k_weight, cos, sin, eps: float) -> Quantized:
+    """Step 0 on Q and K, then steps 1-4 on the results (V unchanged)."""
+    return quantize(norm_rope(Q, q_weight, cos, sin, eps), norm_rope(K, k_weight, cos, sin, eps), V)
 
 
 def qk_s32(qz: Quantized, r0: int = 0, r1: int = None) -> np.ndarray:

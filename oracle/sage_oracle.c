@@ -20,6 +20,8 @@
  *             reciprocal of d, then normalisation, V scale and BF16.
  *   [PAIR]    "Sage2 SM89 Temporal Pair Experiment", section "Candidate": the
  *             per-tile order QK -> update_mdo -> accumulate_d -> RS_32_to_8 -> PV.
+ *   [P1]      "Sage2 Blackwell Mainloop", section "Completed P1 And P2": the
+ *             optional upstream Q/K RMSNorm + split-half RoPE producer.
  *
  * Arithmetic: every floating-point step below is an IEEE binary32 operation
  * (round to nearest even), written one operation per statement.  The file is
@@ -161,6 +163,61 @@ static int8_t int8_code(float x, float inv)
 }
 
 /* ---------------------------------------------------------------- steps -- */
+
+/* Step 0 (optional upstream producer): per-head RMSNorm of Q or K rows, then
+ * split-half rotary position embedding.  [P1] "Sage2 Blackwell Mainloop",
+ * section "Completed P1 And P2": the P1 producer fuses strided-NHD Q/K RMSNorm,
+ * split-half RoPE and Q INT8 quantization, byte-exact with the same steps run
+ * separately; its output feeds steps 1-3 unchanged.
+ * Readings (the pages give neither the normalised span, the weight, epsilon,
+ * the positions nor the roundings):
+ *   - RMSNorm over the 128 channels of one (b, n, h) row with an FP32 weight
+ *     g[128] shared by every head and a caller epsilon eps;
+ *       ss = sum of fl(x_d * x_d) for d = 0..127, sequentially from +0;
+ *       r  = fl(1 / fl(sqrt(fl(fl(ss / 128) + eps))));
+ *       y_d = bf16(fl(fl(x_d * r) * g[d]))   (the normalised row is BF16);
+ *   - split-half rotation (channel i pairs with i + 64) by the caller's FP32
+ *     angle tables cs[N][64], sn[N][64] (row n = token n, every batch and head):
+ *       o_i      = bf16(fl(fl(y_i * c) - fl(y_{i+64} * s)))
+ *       o_{i+64} = bf16(fl(fl(y_{i+64} * c) + fl(y_i * s)))   c = cs[n][i], s = sn[n][i].
+ * Output: BF16 bits [B][N][H][128], contiguous. */
+void oracle_norm_rope(const uint16_t* X, int64_t sb, int64_t sn, int64_t sh,
+                      int B, int N, int H, const float* g, const float* cs, const float* snt,
+                      float eps, uint16_t* out)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int n = 0; n < N; ++n)
+            for (int h = 0; h < H; ++h) {
+                float x[HD], y[HD];
+                float ss = 0.0f;
+                for (int d = 0; d < HD; ++d) {
+                    x[d] = in_val(X, sb, sn, sh, b, n, h, d);
+                    float sq = x[d] * x[d];
+                    ss = ss + sq;
+                }
+                float ms = ss / 128.0f;
+                float t = ms + eps;
+                float w = sqrtf(t);
+                float r = 1.0f / w;
+                for (int d = 0; d < HD; ++d) {
+                    float xr = x[d] * r;
+                    float xg = xr * g[d];
+                    y[d] = oracle_bf16_to_f32(oracle_f32_to_bf16(xg));
+                }
+                uint16_t* o = out + (((int64_t)b * N + n) * H + h) * HD;
+                const float* crow = cs + (int64_t)n * (HD / 2);
+                const float* srow = snt + (int64_t)n * (HD / 2);
+                for (int i = 0; i < HD / 2; ++i) {
+                    float c = crow[i], s = srow[i];
+                    float ac = y[i] * c, bs = y[i + HD / 2] * s;
+                    float bc = y[i + HD / 2] * c, as = y[i] * s;
+                    o[i] = oracle_f32_to_bf16(ac - bs);
+                    o[i + HD / 2] = oracle_f32_to_bf16(bc + as);
+                }
+            }
+}
+
 
 /* Step 1: exact global K channel mean.  [DESIGN, Decision: "K mean/smoothing"];
  * [FLOW: "Keep the exact global K mean"].

@@ -18,6 +18,7 @@ from oracle import build as obuild
 
 import test_oracle_attention as ta
 import test_oracle_codecs as tc
+import test_oracle_norm_rope as tn
 import test_oracle_quant as tq
 
 MUTANTS = {
@@ -47,6 +48,16 @@ MUTANTS = {
     "pv_transposed": ("vdec[v8[(bh * Nk + n) * HD + e]]", "vdec[v8[(bh * Nk + j * BK + e % BK) * HD + cc * 2]]"),
     "no_v_scale": ("float o = (RO[e] * rcp) * vs[e];", "float o = (RO[e] * rcp) * vs[0];"),
     "bf16_truncates": ("u += 0x7fffu + lsb;", "u += 0u * lsb;"),
+    "norm_divides_by_64": ("float ms = ss / 128.0f;", "float ms = ss / 64.0f;"),
+    "norm_no_sqrt": ("float w = sqrtf(t);", "float w = t;"),
+    "norm_no_eps": ("float t = ms + eps;", "float t = ms;"),
+    "norm_no_weight": ("float xg = xr * g[d];", "float xg = xr;"),
+    "norm_sums_abs": ("float sq = x[d] * x[d];", "float sq = fabsf(x[d]);"),
+    "norm_not_rounded": ("y[d] = oracle_bf16_to_f32(oracle_f32_to_bf16(xg));", "y[d] = xg;"),
+    "rope_sign": ("o[i] = oracle_f32_to_bf16(ac - bs);", "o[i] = oracle_f32_to_bf16(ac + bs);"),
+    "rope_pairs_mirror": ("float ac = y[i] * c, bs = y[i + HD / 2] * s;", "float ac = y[i] * c, bs = y[HD - 1 - i] * s;"),
+    "rope_first_token_row": ("const float* crow = cs + (int64_t)n * (HD / 2);", "const float* crow = cs;"),
+    "rope_cos_sin_swapped": ("float c = crow[i], s = srow[i];", "float c = srow[i], s = crow[i];"),
     "qk_skips_last_dim": ("for (int d = 0; d < HD; ++d)\n                        s += (int32_t)q[d] * (int32_t)k[d];\n                    t[cc]",
                           "for (int d = 0; d < HD - 1; ++d)\n                        s += (int32_t)q[d] * (int32_t)k[d];\n                    t[cc]"),
 }
@@ -73,6 +84,12 @@ def _battery():
         ("dominant_key", ta.test_one_dominant_key),
         ("small_weights", ta.test_small_weights_survive_fp8),
         ("qk_s32", lambda o: ta.test_qk_s32_matches_int64_matmul(o, "tiny")),
+        ("nr_pow2", tn.test_power_of_two_rows_give_the_weight),
+        ("nr_eps", tn.test_large_epsilon_on_tiny_rows),
+        ("nr_turns", tn.test_quarter_and_half_turns),
+        ("nr_angles", tn.test_random_angles_against_float64_rotation),
+        ("nr_f64", lambda o: tn.test_against_float64_rmsnorm_and_rotation(o, 1e-6)),
+        ("nr_rounded", tn.test_normalised_row_is_rounded_before_rotation),
     ]
 
 

@@ -13,6 +13,10 @@ Recipe (CPU, ``torch.Generator`` seeded per workload), in this draw order:
   5. outliers (Mid only): randperm(H*128)[:round(0.01*H*128)] channels of K,
      offset included, are multiplied by 8
   6. round each tensor to BF16 (round to nearest even)
+Optional RMSNorm + RoPE parameters (``norm_rope_params``): weights
+1 + 0.2 * randn [128] for Q and for K (FP32), the rotary angle table of 1-D
+positions n = 0..N-1 with frequencies 10000^(-i/64), i = 0..63, evaluated in
+float64 and rounded to FP32, and eps = 1e-6.
 Layouts: "separate" gives three contiguous [B, N, H, 128] tensors;
 "projection" gives three strided views into one BF16 buffer [B, N, 3*H*128]
 (Q, K, V as consecutive column slices), so stride_n = 3*H*128.
@@ -108,6 +112,28 @@ def generate(w: Workload, device: str = "cpu") -> Inputs:
         else:
             views = [t.to(device) for t in views]
     return Inputs(views[0], views[1], views[2], buf)
+
+
+@dataclass
+class NormRopeParams:
+    q_weight: torch.Tensor   # FP32 [128]
+    k_weight: torch.Tensor   # FP32 [128]
+    cos: torch.Tensor        # FP32 [N, 64], row n = token n
+    sin: torch.Tensor        # FP32 [N, 64]
+    eps: float = 1e-6
+
+
+def norm_rope_params(N: int, seed: int = 7, device: str = "cpu") -> NormRopeParams:
+    """Seeded RMSNorm weights and a rotary angle table for N tokens."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    qw = 1.0 + 0.2 * torch.randn(HD, generator=g)
+    kw = 1.0 + 0.2 * torch.randn(HD, generator=g)
+    pos = torch.arange(N, dtype=torch.float64)[:, None]
+    freq = 10000.0 ** (-torch.arange(HD // 2, dtype=torch.float64) / (HD // 2))
+    ang = pos * freq[None, :]
+    cos = torch.cos(ang).to(torch.float32)
+    sin = torch.sin(ang).to(torch.float32)
+    return NormRopeParams(qw.to(device), kw.to(device), cos.to(device), sin.to(device), 1e-6)
 
 
 def with_padding_rows(x: torch.Tensor, extra: int, fill_seed: int = 12345) -> torch.Tensor:
