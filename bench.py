@@ -9,7 +9,9 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
   value       effective TOPS of the whole step: 4*N^2*H*D / step time, the step
               being sage_quantize_qkv + sage_attn_fwd_quantized (events around
               each); the one-call sage_attn_fwd, whose mainloop quantizes Q
-              itself, is timed as well (one_call_ms_per_step)
+              itself, is timed as well (one_call_ms_per_step), and so is the
+              prepass with the optional RMSNorm + RoPE producer on Q and K
+              (norm_rope_prepass_ms; same HBM bytes as the plain prepass)
   roofline    the mainloop kernel: effective ops / its average duration
               (HIP events on the launch stream) against the MI355X dense
               INT8/FP8 matrix peak of 5.0 POP/s; `traffic` is the HBM bytes
@@ -143,6 +145,8 @@ def main():
                     help="input / quantized-operand sets the steps cycle through (cold caches)")
     ap.add_argument("--no-one-call", action="store_true",
                     help="skip timing the one-call path (profiles of the two-call mainloop only)")
+    ap.add_argument("--no-norm-rope", action="store_true",
+                    help="skip timing the prepass with the RMSNorm + RoPE producer")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -252,6 +256,26 @@ def main():
         torch.cuda.synchronize(dev)
         one_call_ms = o_start.elapsed_time(o_end) / args.steps
         log("bench: one-call step %.3f ms" % one_call_ms)
+    # The prepass with the optional RMSNorm + split-half RoPE producer on Q
+    # and K (same outputs as the prepass on the normalised, rotated rows).
+    nr_ms = None
+    if not args.no_norm_rope:
+        p = workloads.norm_rope_params(w.N)
+        nrp = (p.q_weight.to(dev), p.k_weight.to(dev), p.cos.to(dev), p.sin.to(dev))
+        for i in range(args.warmup):
+            q, k, v = qkv[i % args.rotate]
+            sage.quantize_qkv_norm_rope(q, k, v, *nrp, p.eps, into=qzs[i % args.rotate])
+        torch.cuda.synchronize(dev)
+        n_start = torch.cuda.Event(enable_timing=True)
+        n_end = torch.cuda.Event(enable_timing=True)
+        n_start.record(stream)
+        for i in range(args.steps):
+            q, k, v = qkv[i % args.rotate]
+            sage.quantize_qkv_norm_rope(q, k, v, *nrp, p.eps, into=qzs[i % args.rotate])
+        n_end.record(stream)
+        torch.cuda.synchronize(dev)
+        nr_ms = n_start.elapsed_time(n_end) / args.steps
+        log("bench: norm+rope prepass %.3f ms" % nr_ms)
     result = {
         "metric": METRIC,
         "value": ops / (ms_per_step * 1e-3) / 1e12,
@@ -279,6 +303,8 @@ def main():
         "one_call_ms_per_step": one_call_ms,
         "one_call_tops": ops / (one_call_ms * 1e-3) / 1e12 if one_call_ms else None,
         "prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (prep_avg * 1e-3) / 1e9,
+        "norm_rope_prepass_ms": nr_ms,
+        "norm_rope_prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (nr_ms * 1e-3) / 1e9 if nr_ms else None,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
     }

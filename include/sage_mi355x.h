@@ -145,6 +145,36 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
 sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
                               const sage_quantized* qz, void* stream);
 
+/* Parameters of the optional upstream Q/K producer ("Sage2 Blackwell
+ * Mainloop", Completed P1 And P2: strided-NHD Q/K RMSNorm and split-half RoPE
+ * fused with Q INT8 quantization).  Device pointers, FP32, 16-byte aligned:
+ * q_weight, k_weight: the RMSNorm weights [128], shared by every head;
+ * cos, sin: the rotary angle tables [N][64], row n for token n of every batch
+ * entry and head, column i for the channel pair (i, i + 64).  eps > 0. */
+typedef struct sage_norm_rope {
+    const float* q_weight;
+    const float* k_weight;
+    const float* cos;
+    const float* sin;
+    float eps;
+} sage_norm_rope;
+
+/* sage_quantize_qkv applied to Q' and K' instead of Q and K, where for each
+ * (b, n, h) row x of Q (weight q_weight) or K (weight k_weight):
+ *   ss = sum over channels c = 0..127, in order, of fl(x_c * x_c), from +0
+ *   r  = fl(1 / fl(sqrt(fl(fl(ss / 128) + eps))))
+ *   y_c = bf16(fl(fl(x_c * r) * weight[c]))                   (RNE)
+ *   x'_i = bf16(fl(fl(y_i * cos[n][i]) - fl(y_{i+64} * sin[n][i])))
+ *   x'_{i+64} = bf16(fl(fl(y_{i+64} * cos[n][i]) + fl(y_i * sin[n][i])))  (i < 64)
+ * V is used as is.  Q' and K' are never stored: the prepass recomputes them
+ * from Q and K where it reads them, so the outputs are byte-identical to
+ * sage_quantize_qkv on Q', K' and the memory traffic is that of
+ * sage_quantize_qkv.  Errors: as sage_quantize_qkv; INVALID_ARGUMENT when nr
+ * or one of its pointers is NULL or eps is not finite and > 0; UNSUPPORTED
+ * when a table or weight pointer is not 16-byte aligned. */
+sage_status sage_quantize_qkv_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                        const sage_norm_rope* nr, const sage_quantized* qz, void* stream);
+
 /* The fused mainloop and epilogue ("State-Ownership Architecture Decision",
  * Non-Negotiable Dataflow).  For every query row, over K/V tiles t = 0..T-1:
  *   S = q_i8 . k_i8^T (exact int32);  t = S * (q_scale*k_scale*sm_scale*log2 e)

@@ -15,7 +15,7 @@ import os
 from . import build as _build
 
 __all__ = [
-    "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv",
+    "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv", "quantize_qkv_norm_rope",
     "attn_fwd_quantized", "attn_fwd", "debug_qk_s32", "debug_cvt_e4m3", "default_sm_scale",
 ]
 
@@ -53,6 +53,11 @@ class _Quantized(ctypes.Structure):
                 ("k_tile_sum", ctypes.c_void_p), ("v_tile_amax", ctypes.c_void_p), ("v_inv", ctypes.c_void_p)]
 
 
+class _NormRope(ctypes.Structure):
+    _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -76,6 +81,9 @@ def _load():
     lib.sage_quantized_carve.restype = st
     lib.sage_quantize_qkv.argtypes = [ctypes.POINTER(_In)] * 3 + [ctypes.POINTER(_Quantized), P]
     lib.sage_quantize_qkv.restype = st
+    lib.sage_quantize_qkv_norm_rope.argtypes = [ctypes.POINTER(_In)] * 3 + [ctypes.POINTER(_NormRope),
+                                                                           ctypes.POINTER(_Quantized), P]
+    lib.sage_quantize_qkv_norm_rope.restype = st
     lib.sage_attn_fwd_quantized.argtypes = [ctypes.POINTER(_Quantized), ctypes.c_float, ctypes.POINTER(_Out), P]
     lib.sage_attn_fwd_quantized.restype = st
     lib.sage_attn_fwd_quantized_range.argtypes = [ctypes.POINTER(_Quantized), ctypes.c_float,
@@ -210,24 +218,53 @@ class Quantized:
         return self._view("v_scale", _torch().float32, self.B * self.H * HEAD_DIM).view(self.B, self.H, HEAD_DIM)
 
 
-def quantize_qkv(q, k, v, workspace=None, into: Quantized = None) -> Quantized:
-    """The prepass: K mean, INT8 Q/K and FP8 V with their scales.
-
-    With ``into``, the operands are rewritten in that object's workspace
-    (same shape required) and nothing is allocated."""
-    dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
+def _target(q, k, v, workspace, into):
     if not (q.shape == k.shape == v.shape):
         raise SageError("q, k, v shapes differ")
     B, N, H, _ = q.shape
     if into is not None:
         if (into.B, into.N, into.H) != (B, N, H):
             raise SageError("into has shape %s, inputs %s" % ((into.B, into.N, into.H), (B, N, H)))
-        qz = into
-    else:
-        qz = Quantized(B, N, H, q.device, workspace)
+        return into
+    return Quantized(B, N, H, q.device, workspace)
+
+
+def quantize_qkv(q, k, v, workspace=None, into: Quantized = None) -> Quantized:
+    """The prepass: K mean, INT8 Q/K and FP8 V with their scales.
+
+    With ``into``, the operands are rewritten in that object's workspace
+    (same shape required) and nothing is allocated."""
+    dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
+    qz = _target(q, k, v, workspace, into)
     _check(_load().sage_quantize_qkv(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                                      ctypes.byref(qz.c), _stream_ptr(q)))
     qz._inputs = (q, k, v)
+    return qz
+
+
+def _f32_desc(x, shape, name):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32 \
+            or tuple(x.shape) != tuple(shape) or not x.is_contiguous():
+        raise SageError("%s must be a contiguous FP32 GPU tensor of shape %s" % (name, tuple(shape)))
+    return x.data_ptr()
+
+
+def quantize_qkv_norm_rope(q, k, v, q_weight, k_weight, cos, sin, eps: float = 1e-6,
+                           workspace=None, into: Quantized = None) -> Quantized:
+    """The prepass on RMSNorm + split-half RoPE of Q and K (V as is).
+
+    q_weight, k_weight: FP32 [128]; cos, sin: FP32 [N, 64] (row n = token n).
+    The normalised and rotated rows are recomputed where the prepass reads Q
+    and K and never stored; the result equals quantize_qkv on them."""
+    dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
+    N = q.shape[1]
+    nr = _NormRope(_f32_desc(q_weight, (HEAD_DIM,), "q_weight"), _f32_desc(k_weight, (HEAD_DIM,), "k_weight"),
+                   _f32_desc(cos, (N, HEAD_DIM // 2), "cos"), _f32_desc(sin, (N, HEAD_DIM // 2), "sin"), eps)
+    qz = _target(q, k, v, workspace, into)
+    _check(_load().sage_quantize_qkv_norm_rope(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                               ctypes.byref(nr), ctypes.byref(qz.c), _stream_ptr(q)))
+    qz._inputs = (q, k, v, q_weight, k_weight, cos, sin)
     return qz
 
 

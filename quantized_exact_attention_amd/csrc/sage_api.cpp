@@ -118,8 +118,20 @@ sage_status hip_status(hipError_t e, const char* what) {
     return SAGE_OK;
 }
 
+sage_status check_norm_rope(const sage_norm_rope* nr) {
+    if (!nr) return fail(SAGE_ERR_INVALID_ARGUMENT, "norm/rope descriptor is NULL");
+    if (!nr->q_weight || !nr->k_weight || !nr->cos || !nr->sin)
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "a norm/rope weight or table pointer is NULL");
+    const void* p16[] = {nr->q_weight, nr->k_weight, nr->cos, nr->sin};
+    for (const void* p : p16)
+        if ((uintptr_t)p % 16) return fail(SAGE_ERR_UNSUPPORTED, "norm/rope weights and tables must be 16-byte aligned");
+    if (!std::isfinite(nr->eps) || !(nr->eps > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+    return SAGE_OK;
+}
+
 sage_status prepass(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
-                    const sage_quantized* qz, bool with_q, void* stream) {
+                    const sage_quantized* qz, bool with_q, const sage_norm_rope* nr, void* stream) {
     Dims d;
     sage_status st;
     if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
@@ -136,6 +148,9 @@ sage_status prepass(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf1
     p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_mean = qz->k_mean;
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.k_tile_sum = qz->k_tile_sum; p.v_tile_amax = qz->v_tile_amax; p.v_inv = qz->v_inv;
+    p.norm_rope = nr != nullptr;
+    p.nr = sage::NormRopeArgs{nullptr, nullptr, nullptr, nullptr, 0.0f};
+    if (nr) p.nr = sage::NormRopeArgs{nr->q_weight, nr->k_weight, nr->cos, nr->sin, nr->eps};
     return hip_status(sage::launch_prepass(p, (hipStream_t)stream), "prepass launch");
 }
 
@@ -240,7 +255,15 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
 sage_status sage_quantize_qkv(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
                               const sage_quantized* qz, void* stream) {
     clear_err();
-    return prepass(q, k, v, qz, true, stream);
+    return prepass(q, k, v, qz, true, nullptr, stream);
+}
+
+sage_status sage_quantize_qkv_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                        const sage_norm_rope* nr, const sage_quantized* qz, void* stream) {
+    clear_err();
+    sage_status st;
+    if ((st = check_norm_rope(nr)) != SAGE_OK) return st;
+    return prepass(q, k, v, qz, true, nr, stream);
 }
 
 sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
@@ -270,7 +293,7 @@ sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sa
         return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
     if ((st = check_in(q, "q")) != SAGE_OK) return st;
     // K and V through the prepass; Q is quantized inside the mainloop.
-    if ((st = prepass(q, k, v, &qz, false, stream)) != SAGE_OK) return st;
+    if ((st = prepass(q, k, v, &qz, false, nullptr, stream)) != SAGE_OK) return st;
     const sage_range all = {0, s.N, 0, s.H};
     return mainloop(&qz, sm_scale, &all, o, q, stream);
 }

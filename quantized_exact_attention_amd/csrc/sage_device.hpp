@@ -85,18 +85,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // the 16 codes it owns in the operand layout of the QK instruction.  The
 // group scale is amax/127 and each code rne(x * (127/amax)) clamped to
 // +-127; a group with amax < 2^-100 gets scale 0 and zero codes.
-__device__ __forceinline__ float quant_q_group(const uint16_t* row, bool valid, uint4 (&codes)[4]) {
-    float x[64];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
-        if (valid) {
-            w0 = *(const uint4*)(row + 32 * kk);
-            w1 = *(const uint4*)(row + 32 * kk + 8);
-        }
-        unpack8(w0, x + 16 * kk);
-        unpack8(w1, x + 16 * kk + 8);
-    }
+__device__ __forceinline__ float quant_q_values(const float (&x)[64], uint4 (&codes)[4]) {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) am = fmaxf(am, fabsf(x[i]));
@@ -109,6 +98,147 @@ __device__ __forceinline__ float quant_q_group(const uint16_t* row, bool valid, 
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) codes[kk] = pack16_int8(x + 16 * kk, inv);
     return scale;
+}
+
+// quant_q_values on a row kept as packed BF16 words w[8] (w[2kk + e] holds
+// the lane's channels 32kk + 16*(l/32) + 8e + 0..7): the words are widened
+// twice, once for the maximum and once for the codes, so that no 64-float
+// copy of the row stays live.  Same results as quant_q_values.
+__device__ __forceinline__ float quant_q_words(const uint4 (&w)[8], uint4 (&codes)[4]) {
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float x[8];
+        unpack8(w[j], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+    }
+    am = wave_max(am);
+    float scale = 0.0f, inv = 0.0f;
+    if (am >= kAmaxFloor) {
+        scale = am / 127.0f;
+        inv = 127.0f / am;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        float x[16];
+        unpack8(w[2 * kk], x);
+        unpack8(w[2 * kk + 1], x + 8);
+        codes[kk] = pack16_int8(x, inv);
+    }
+    return scale;
+}
+
+__device__ __forceinline__ float quant_q_group(const uint16_t* row, bool valid, uint4 (&codes)[4]) {
+    float x[64];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
+        if (valid) {
+            w0 = *(const uint4*)(row + 32 * kk);
+            w1 = *(const uint4*)(row + 32 * kk + 8);
+        }
+        unpack8(w0, x + 16 * kk);
+        unpack8(w1, x + 16 * kk + 8);
+    }
+    return quant_q_values(x, codes);
+}
+
+// FP32 -> BF16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    const v2bf t = v2bf{(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, t);
+}
+
+__device__ __forceinline__ uint32_t& word_of(uint4& w, int m) {
+    return m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w;
+}
+
+// Optional upstream producer ("Sage2 Blackwell Mainloop", Completed P1 And
+// P2): per-head RMSNorm of one Q or K row, then split-half rotary embedding,
+// each result rounded to BF16, in place on the row's BF16 words.  The row is
+// held by lanes l%32 and l%32 + 32 of a wave in the QK operand split: on the
+// lane with hf = l/32, w[2kk + e] holds channels 32kk + 16hf + 8e + 0..7.
+//   ss  = sum over channels 0..127 in order of fl(x*x), from +0 (both lanes
+//         see both halves through v_permlane32_swap and sum identically)
+//   r   = fl(1 / fl(sqrt(fl(fl(ss / 128) + eps))))
+//   y_c = bf16(fl(fl(x_c * r) * g[c]))
+//   o_i = bf16(fl(fl(y_i * cos_i) - fl(y_{i+64} * sin_i))),
+//   o_{i+64} = bf16(fl(fl(y_{i+64} * cos_i) + fl(y_i * sin_i))), i < 64,
+// with the angle row (cos_row, sin_row: 64 FP32 each) of the row's token.
+// Channel i and i + 64 sit on the same lane (kk and kk + 2).
+__device__ __forceinline__ void norm_rope_row(uint4 (&w)[8], int hf, const float* g, const float* cos_row,
+                                              const float* sin_row, float eps) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint32_t h0[8], h1[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t u = word_of(w[2 * kk + m / 4], m % 4);
+            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            h0[m] = r[0];
+            h1[m] = r[1];
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float a = __uint_as_float(h0[m] << 16), b = __uint_as_float(h0[m] & 0xffff0000u);
+            const float a2 = a * a;
+            ss = ss + a2;
+            const float b2 = b * b;
+            ss = ss + b2;
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float a = __uint_as_float(h1[m] << 16), b = __uint_as_float(h1[m] & 0xffff0000u);
+            const float a2 = a * a;
+            ss = ss + a2;
+            const float b2 = b * b;
+            ss = ss + b2;
+        }
+    }
+    const float ms = ss / 128.0f;
+    const float t = ms + eps;
+    const float rt = sqrtf(t);
+    const float r = 1.0f / rt;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        // channels c = 32kk + 16hf + j (first half) and c + 64 (second half)
+        float y0[16], y1[16];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = 8 * e + 2 * m;
+                const int c = 32 * kk + 16 * hf + j;
+                const uint32_t u0 = word_of(w[2 * kk + e], m), u1 = word_of(w[2 * kk + 4 + e], m);
+                const float x00 = __uint_as_float(u0 << 16), x01 = __uint_as_float(u0 & 0xffff0000u);
+                const float x10 = __uint_as_float(u1 << 16), x11 = __uint_as_float(u1 & 0xffff0000u);
+                float p;
+                p = x00 * r; p = p * g[c];          y0[j] = (float)(__bf16)p;
+                p = x01 * r; p = p * g[c + 1];      y0[j + 1] = (float)(__bf16)p;
+                p = x10 * r; p = p * g[c + 64];     y1[j] = (float)(__bf16)p;
+                p = x11 * r; p = p * g[c + 65];     y1[j + 1] = (float)(__bf16)p;
+            }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = 8 * e + 2 * m;
+                const int i = 32 * kk + 16 * hf + j;
+                float o0[2], o1[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float c = cos_row[i + q], s = sin_row[i + q];
+                    const float ac = y0[j + q] * c, bs = y1[j + q] * s;
+                    const float bc = y1[j + q] * c, as = y0[j + q] * s;
+                    o0[q] = ac - bs;
+                    o1[q] = bc + as;
+                }
+                word_of(w[2 * kk + e], m) = bf16x2_bits(o0[0], o0[1]);
+                word_of(w[2 * kk + 4 + e], m) = bf16x2_bits(o1[0], o1[1]);
+            }
+    }
 }
 
 // Maximum of the 32 int32 values of two accumulator tiles (two chains, so

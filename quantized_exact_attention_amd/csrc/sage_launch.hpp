@@ -6,6 +6,15 @@
 
 namespace sage {
 
+// Optional RMSNorm + RoPE producer parameters (device pointers).
+struct NormRopeArgs {
+    const float* q_weight;   // [128]
+    const float* k_weight;   // [128]
+    const float* cos;        // [N][64], row n = token n
+    const float* sin;        // [N][64]
+    float eps;
+};
+
 struct StatsArgs {
     const uint16_t* k; int64_t k_sb, k_sn, k_sh;
     const uint16_t* v; int64_t v_sb, v_sn, v_sh;
@@ -13,6 +22,7 @@ struct StatsArgs {
     int64_t units;
     float* k_tile_sum;
     float* v_tile_amax;
+    NormRopeArgs nr;
 };
 
 struct FinalizeArgs {
@@ -36,6 +46,7 @@ struct QuantArgs {
     int8_t* q_i8; float* q_scale;
     int8_t* k_i8; float* k_scale;
     uint8_t* v_fp8;
+    NormRopeArgs nr;
 };
 
 struct PrepassArgs {
@@ -48,6 +59,8 @@ struct PrepassArgs {
     int8_t* k_i8; float* k_scale; float* k_mean;
     uint8_t* v_fp8; float* v_scale;
     float* k_tile_sum; float* v_tile_amax; float* v_inv;
+    bool norm_rope;      // apply the RMSNorm + RoPE producer to Q and K first
+    NormRopeArgs nr;
 };
 
 // Query groups (32 rows, one wavefront each) per mainloop workgroup.

@@ -171,3 +171,26 @@ def test_range_validation_happens_before_launch(sage):
         assert b"range" in lib.sage_last_error_message()
     assert lib.sage_attn_fwd_quantized_range(ctypes.byref(qz), ctypes.c_float(0.088), None,
                                              ctypes.byref(out), None) == 1
+
+
+def test_norm_rope_validation_happens_before_launch(sage):
+    """The RMSNorm + RoPE prepass rejects a missing descriptor, missing or
+    misaligned weights and tables, and a bad epsilon, without a launch."""
+    lib = sage._load()
+    qz = _carved(sage)
+    good = sage._In(0x7e0000000000, 200 * 2 * 128, 2 * 128, 128)
+    B = ctypes.byref
+    w, c, s = 0x7a0000000000, 0x7a0000100000, 0x7a0000200000
+    assert lib.sage_quantize_qkv_norm_rope(B(good), B(good), B(good), None, B(qz), None) == 1
+    assert b"descriptor" in lib.sage_last_error_message()
+    for nr, code in ((sage._NormRope(None, w, c, s, 1e-6), 1), (sage._NormRope(w, w, None, s, 1e-6), 1),
+                     (sage._NormRope(w + 4, w, c, s, 1e-6), 2), (sage._NormRope(w, w, c, s + 8, 1e-6), 2),
+                     (sage._NormRope(w, w, c, s, 0.0), 1), (sage._NormRope(w, w, c, s, -1e-6), 1),
+                     (sage._NormRope(w, w, c, s, float("nan")), 1), (sage._NormRope(w, w, c, s, float("inf")), 1)):
+        assert lib.sage_quantize_qkv_norm_rope(B(good), B(good), B(good), B(nr), B(qz), None) == code
+    ok = sage._NormRope(w, w, c, s, 1e-6)
+    null = sage._In(None, 0, 0, 0)
+    assert lib.sage_quantize_qkv_norm_rope(B(null), B(good), B(good), B(ok), B(qz), None) == 1
+    bad_shape = _carved(sage)
+    bad_shape.shape.D = 64
+    assert lib.sage_quantize_qkv_norm_rope(B(good), B(good), B(good), B(ok), B(bad_shape), None) == 1

@@ -1,0 +1,119 @@
+"""GPU parity of the prepass with the optional RMSNorm + split-half RoPE
+producer ("Sage2 Blackwell Mainloop", Completed P1 And P2) against the oracle.
+
+Bar: every quantized byte, every scale and the K mean bit-identical to the
+oracle's steps 0-4 (normalise and rotate Q and K, then quantize); the BF16
+attention output on those operands within max |diff| 2e-2 and cosine 0.9999.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import layouts
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MIN_COS = 0.9999
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_exact_attention_amd as s
+    s._load()
+    return s
+
+
+@functools.lru_cache(maxsize=1)
+def _case(name, B=None):
+    import oracle
+    w = workloads.by_name(name)
+    if B is not None:
+        w = workloads.Workload(w.name + "_b%d" % B, B, w.N, w.H, seed=w.seed + 50, layout="projection")
+    inp = workloads.generate(w)
+    p = workloads.norm_rope_params(w.N, seed=w.seed + 9)
+    ref = oracle.quantize_norm_rope(inp.q, inp.k, inp.v, p.q_weight, p.k_weight, p.cos, p.sin, p.eps)
+    return w, inp, p, ref
+
+
+def _to_gpu(inp):
+    if inp.buffer is not None:
+        buf = inp.buffer.cuda()
+        B, N, H = inp.q.shape[:3]
+        return tuple(buf[:, :, i * H * 128:(i + 1) * H * 128].view(B, N, H, 128) for i in range(3))
+    return inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+
+
+def _bits(x):
+    return np.asarray(x).view(np.uint32)
+
+
+def _run(sage, inp, p):
+    q, k, v = _to_gpu(inp)
+    qz = sage.quantize_qkv_norm_rope(q, k, v, p.q_weight.cuda(), p.k_weight.cuda(), p.cos.cuda(), p.sin.cuda(),
+                                     p.eps)
+    torch.cuda.synchronize()
+    return qz
+
+
+def _check_bytes(qz, ref, w):
+    B, N, H = w.B, w.N, w.H
+    assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
+    assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    gq = layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gq, ref.q_i8), "q_i8 differs in %d bytes" % int((gq != ref.q_i8).sum())
+    gk = layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gk, ref.k_i8), "k_i8 differs in %d bytes" % int((gk != ref.k_i8).sum())
+    gv = layouts.v_logical(qz.v_fp8.cpu().numpy(), B, H, N)
+    assert np.array_equal(gv, ref.v8), "v_fp8 differs in %d bytes" % int((gv != ref.v8).sum())
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep_n65", "sweep_n127", "sweep_n129", "mid", "large", "canonical"])
+def test_norm_rope_quantized_bytes_bit_exact(sage, name):
+    _log("norm_rope quant parity: %s" % name)
+    w, inp, p, ref = _case(name)
+    _check_bytes(_run(sage, inp, p), ref, w)
+
+
+def test_norm_rope_batched_projection_bit_exact(sage):
+    _log("norm_rope quant parity: B=2 projection")
+    w, inp, p, ref = _case("sweep_n129", B=2)
+    _check_bytes(_run(sage, inp, p), ref, w)
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep_n129", "mid"])
+def test_norm_rope_attention_parity(sage, name):
+    import oracle
+    _log("norm_rope attention parity: %s" % name)
+    w, inp, p, ref = _case(name)
+    qz = _run(sage, inp, p)
+    out = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    if w.N * w.H <= 4096:
+        rows = [(0, h, n) for h in range(w.H) for n in range(w.N)]
+    else:
+        rows = [(0, h, int(n)) for h in range(w.H)
+                for n in np.concatenate([np.arange(32), np.arange(w.N - 40, w.N), rng.integers(0, w.N, 40)])]
+    rows = np.array(rows, np.int64)
+    bits, _ = oracle.attn_rows(ref, rows)
+    got = out.float().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+    refv = oracle.bf16_decode(bits)
+    max_abs = float(np.max(np.abs(got - refv)))
+    a, b = got.astype(np.float64).ravel(), refv.astype(np.float64).ravel()
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    _log("  rows=%d max_abs=%.3g cos=%.7f" % (len(rows), max_abs, cos))
+    assert max_abs <= MAX_ABS and cos >= MIN_COS
