@@ -36,11 +36,14 @@ def sage():
 
 
 @functools.lru_cache(maxsize=1)
-def _case(name, B=None):
+def _case(name, B=None, layout="projection"):
     import oracle
-    w = workloads.by_name(name)
+    if name.startswith("n="):
+        w = workloads.Workload(name, 1, int(name[2:]), 3, seed=500 + int(name[2:]))
+    else:
+        w = workloads.by_name(name)
     if B is not None:
-        w = workloads.Workload(w.name + "_b%d" % B, B, w.N, w.H, seed=w.seed + 50, layout="projection")
+        w = workloads.Workload(w.name + "_b%d" % B, B, w.N, w.H, seed=w.seed + 50, layout=layout)
     inp = workloads.generate(w)
     p = workloads.norm_rope_params(w.N, seed=w.seed + 9)
     ref = oracle.quantize_norm_rope(inp.q, inp.k, inp.v, p.q_weight, p.k_weight, p.cos, p.sin, p.eps)
@@ -88,9 +91,17 @@ def test_norm_rope_quantized_bytes_bit_exact(sage, name):
     _check_bytes(_run(sage, inp, p), ref, w)
 
 
-def test_norm_rope_batched_projection_bit_exact(sage):
-    _log("norm_rope quant parity: B=2 projection")
-    w, inp, p, ref = _case("sweep_n129", B=2)
+@pytest.mark.parametrize("layout", ["projection", "separate"])
+def test_norm_rope_batched_bit_exact(sage, layout):
+    _log("norm_rope quant parity: B=2 %s" % layout)
+    w, inp, p, ref = _case("sweep_n129", B=2, layout=layout)
+    _check_bytes(_run(sage, inp, p), ref, w)
+
+
+@pytest.mark.parametrize("n", [1, 2, 33])
+def test_norm_rope_short_sequences_bit_exact(sage, n):
+    _log("norm_rope quant parity: N=%d" % n)
+    w, inp, p, ref = _case("n=%d" % n)
     _check_bytes(_run(sage, inp, p), ref, w)
 
 
