@@ -218,6 +218,17 @@ def test_deterministic_and_two_call_path_identical(sage):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+def test_one_call_equals_two_call_path_canonical(sage):
+    """At the full long-context shape, the one-call path (Q quantized inside
+    the mainloop) writes the same bytes as quantize + mainloop."""
+    _log("one-call vs two-call: canonical")
+    q, k, v = _to_gpu(_cpu_inputs("canonical"))
+    a = sage.attn_fwd(q, k, v)
+    c = sage.attn_fwd_quantized(sage.quantize_qkv(q, k, v))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
 def test_output_strides_and_untouched_memory(sage):
     q, k, v = _to_gpu(_cpu_inputs("sweep_n129"))
     ref = sage.attn_fwd(q, k, v)
