@@ -17,7 +17,11 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
               INT8/FP8 matrix peak of 5.0 POP/s; `traffic` is the HBM bytes
               per launch measured with hardware counters and stored in
               profiles/mainloop_canonical_hbm.md, reported only while the
-              kernel sources still hash to the value recorded there
+              kernel sources still hash to the value recorded there;
+              `mainloop_pipes` gives the counter-measured MFMA busy and VALU
+              active shares and the matrix ops per active cycle (at the clock
+              the chip actually ran) from profiles/mainloop_canonical_counters.md,
+              under the same condition
   cpu_baseline the CPU oracle on a bounded sample of the same workload
               (one head's prepass plus whole query rows of that head over
               all keys), extrapolated to the full workload
@@ -40,6 +44,7 @@ HD = 128
 
 KERNEL_SOURCES = ("attn_mainloop.hip", "sage_device.hpp", "sage_launch.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mainloop_canonical_hbm.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mainloop_canonical_counters.md")
 
 
 def kernel_source_hash():
@@ -50,25 +55,39 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per mainloop launch from the committed counter summary, or
-    None when it is missing, for another workload, or for other sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded_fields(path, workload, names):
+    """Values recorded with hardware counters in a committed summary, or None
+    when it is missing, for another workload, or for other kernel sources."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
-            line = line.strip().strip("`")
-            if ":" in line and line.split(":", 1)[0] in ("kernel_source_sha256", "workload",
-                                                          "hbm_bytes_per_launch"):
+            line = line.strip()
+            if ":" in line and line.split(":", 1)[0] in ("kernel_source_sha256", "workload") + tuple(names):
                 k, v = line.split(":", 1)
-                fields[k] = v.strip()
+                fields[k] = v.strip().strip("`")
     if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return {n: float(fields[n]) for n in names}
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic(workload):
+    """HBM bytes per mainloop launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy
+    of known size), or None."""
+    r = recorded_fields(TRAFFIC_FILE, workload, ("hbm_bytes_per_launch",))
+    return r["hbm_bytes_per_launch"] if r else None
+
+
+def recorded_pipes(workload):
+    """MFMA busy share of SIMD cycles, matrix ops per active cycle against the
+    dense peak (at the clock the chip actually ran), and VALU active share of
+    the mainloop, from the committed counter summary, or None."""
+    return recorded_fields(COUNTERS_FILE, workload,
+                           ("mfma_busy_frac", "mfma_ops_per_active_cycle_frac", "valu_active_frac"))
 
 
 def log(msg):
@@ -307,6 +326,7 @@ def main():
         "norm_rope_prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (nr_ms * 1e-3) / 1e9 if nr_ms else None,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
+        "mainloop_pipes": recorded_pipes(w.name),
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
