@@ -194,3 +194,29 @@ def test_norm_rope_validation_happens_before_launch(sage):
     bad_shape = _carved(sage)
     bad_shape.shape.D = 64
     assert lib.sage_quantize_qkv_norm_rope(B(good), B(good), B(good), B(ok), B(bad_shape), None) == 1
+
+
+def test_error_messages_are_per_thread(sage):
+    """The last-error text is thread-local: concurrent failing calls on two
+    host threads each read back their own message."""
+    import threading
+    lib = sage._load()
+    results = {}
+    barrier = threading.Barrier(2)
+
+    def worker(name, shape):
+        qz = sage._Quantized()
+        for _ in range(200):
+            barrier.wait()
+            st = lib.sage_quantized_carve(shape, 0x7f0000000000, 1 << 40, ctypes.byref(qz))
+            barrier.wait()
+            results.setdefault(name, set()).add((st, lib.sage_last_error_message()))
+
+    t1 = threading.Thread(target=worker, args=("d", sage._Shape(1, 200, 2, 64)))         # bad head dim
+    t2 = threading.Thread(target=worker, args=("n", sage._Shape(1, 0, 2, 128)))          # empty sequence
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert len(results["d"]) == 1 and len(results["n"]) == 1
+    (sd, md), = results["d"]
+    (sn, mn), = results["n"]
+    assert sd == sn == 1
+    assert b"D=64" in md and b"N=0" in mn

@@ -229,6 +229,23 @@ def test_one_call_equals_two_call_path_canonical(sage):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+def test_calls_on_a_non_default_stream(sage):
+    """Every launch goes to the caller's current stream: the whole path on a
+    second stream (default priority) gives the same bytes as on the default
+    one."""
+    q, k, v = _to_gpu(_cpu_inputs("sweep_n129"))
+    ref = sage.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qz = sage.quantize_qkv(q, k, v)
+        two = sage.attn_fwd_quantized(qz)
+        one = sage.attn_fwd(q, k, v)
+    s.synchronize()
+    assert torch.equal(two.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(one.view(torch.int16), ref.view(torch.int16))
+
+
 def test_output_strides_and_untouched_memory(sage):
     q, k, v = _to_gpu(_cpu_inputs("sweep_n129"))
     ref = sage.attn_fwd(q, k, v)
