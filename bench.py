@@ -11,7 +11,8 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
               each); the one-call sage_attn_fwd, whose mainloop quantizes Q
               itself, is timed as well (one_call_ms_per_step), and so is the
               prepass with the optional RMSNorm + RoPE producer on Q and K
-              (norm_rope_prepass_ms; same HBM bytes as the plain prepass)
+              (norm_rope_prepass_ms; same HBM bytes as the plain prepass),
+              and the one-call path with it (norm_rope_one_call_ms_per_step)
   roofline    the mainloop kernel: effective ops / its average duration
               (HIP events on the launch stream) against the MI355X dense
               INT8/FP8 matrix peak of 5.0 POP/s; `traffic` is the HBM bytes
@@ -277,7 +278,7 @@ def main():
         log("bench: one-call step %.3f ms" % one_call_ms)
     # The prepass with the optional RMSNorm + split-half RoPE producer on Q
     # and K (same outputs as the prepass on the normalised, rotated rows).
-    nr_ms = None
+    nr_ms = nr_one_ms = None
     if not args.no_norm_rope:
         p = workloads.norm_rope_params(w.N)
         nrp = (p.q_weight.to(dev), p.k_weight.to(dev), p.cos.to(dev), p.sin.to(dev))
@@ -295,6 +296,19 @@ def main():
         torch.cuda.synchronize(dev)
         nr_ms = n_start.elapsed_time(n_end) / args.steps
         log("bench: norm+rope prepass %.3f ms" % nr_ms)
+        if not args.no_one_call:
+            for i in range(args.warmup):
+                q, k, v = qkv[i % args.rotate]
+                sage.attn_fwd_norm_rope(q, k, v, *nrp, p.eps, out=out1, workspace=wsv)
+            torch.cuda.synchronize(dev)
+            n_start.record(stream)
+            for i in range(args.steps):
+                q, k, v = qkv[i % args.rotate]
+                sage.attn_fwd_norm_rope(q, k, v, *nrp, p.eps, out=out1, workspace=wsv)
+            n_end.record(stream)
+            torch.cuda.synchronize(dev)
+            nr_one_ms = n_start.elapsed_time(n_end) / args.steps
+            log("bench: norm+rope one-call step %.3f ms" % nr_one_ms)
     result = {
         "metric": METRIC,
         "value": ops / (ms_per_step * 1e-3) / 1e12,
@@ -323,6 +337,7 @@ def main():
         "one_call_tops": ops / (one_call_ms * 1e-3) / 1e12 if one_call_ms else None,
         "prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (prep_avg * 1e-3) / 1e9,
         "norm_rope_prepass_ms": nr_ms,
+        "norm_rope_one_call_ms_per_step": nr_one_ms,
         "norm_rope_prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (nr_ms * 1e-3) / 1e9 if nr_ms else None,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},

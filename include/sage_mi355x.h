@@ -219,6 +219,19 @@ sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sa
                           sage_shape s, float sm_scale, const sage_bf16_out* o,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* sage_attn_fwd with the RMSNorm + split-half RoPE producer of
+ * sage_quantize_qkv_norm_rope (same arithmetic, same parameters): K is
+ * normalised and rotated inside the prepass and Q inside the mainloop, which
+ * normalises, rotates and quantizes each 32-row group in its prologue (the
+ * pages' P1 producer embedded to feed the slots: "Sage2 Blackwell Mainloop",
+ * Completed P1 And P2; "State-Ownership Architecture Decision", VEA-B).  The
+ * output is identical to sage_quantize_qkv_norm_rope +
+ * sage_attn_fwd_quantized.  Errors: as sage_attn_fwd and
+ * sage_quantize_qkv_norm_rope. */
+sage_status sage_attn_fwd_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                    sage_shape s, const sage_norm_rope* nr, float sm_scale,
+                                    const sage_bf16_out* o, void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* sage_status_string(sage_status st);
 

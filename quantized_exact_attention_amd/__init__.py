@@ -16,7 +16,7 @@ from . import build as _build
 
 __all__ = [
     "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv", "quantize_qkv_norm_rope",
-    "attn_fwd_quantized", "attn_fwd", "debug_qk_s32", "debug_cvt_e4m3", "default_sm_scale",
+    "attn_fwd_quantized", "attn_fwd", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3", "default_sm_scale",
 ]
 
 HEAD_DIM = 128
@@ -92,6 +92,10 @@ def _load():
     lib.sage_attn_fwd.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.c_float, ctypes.POINTER(_Out),
                                                               P, ctypes.c_size_t, P]
     lib.sage_attn_fwd.restype = st
+    lib.sage_attn_fwd_norm_rope.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.POINTER(_NormRope),
+                                                                        ctypes.c_float, ctypes.POINTER(_Out),
+                                                                        P, ctypes.c_size_t, P]
+    lib.sage_attn_fwd_norm_rope.restype = st
     lib.sage_status_string.argtypes = [st]
     lib.sage_status_string.restype = ctypes.c_char_p
     lib.sage_last_error_message.argtypes = []
@@ -298,8 +302,7 @@ def attn_fwd_quantized_range(qz: Quantized, q_start: int, q_count: int, head_sta
     return out
 
 
-def attn_fwd(q, k, v, sm_scale: float = None, out=None, workspace=None):
-    """Whole path (prepass + mainloop) in one call; returns BF16 [B, N, H, 128]."""
+def _one_call(q, k, v, sm_scale, out, workspace, nr):
     torch = _torch()
     dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
     if not (q.shape == k.shape == v.shape):
@@ -314,10 +317,28 @@ def attn_fwd(q, k, v, sm_scale: float = None, out=None, workspace=None):
         ws, off, n = _workspace(B, N, H, q.device)
     else:
         ws, off, n = workspace, 0, workspace.numel() * workspace.element_size()
-    _check(_load().sage_attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _Shape(B, N, H, HEAD_DIM),
-                                 ctypes.c_float(sm_scale), ctypes.byref(do), ws.data_ptr() + off, n,
-                                 _stream_ptr(q)))
+    args = (ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _Shape(B, N, H, HEAD_DIM))
+    tail = (ctypes.c_float(sm_scale), ctypes.byref(do), ws.data_ptr() + off, n, _stream_ptr(q))
+    if nr is None:
+        _check(_load().sage_attn_fwd(*args, *tail))
+    else:
+        _check(_load().sage_attn_fwd_norm_rope(*args, ctypes.byref(nr), *tail))
     return out
+
+
+def attn_fwd(q, k, v, sm_scale: float = None, out=None, workspace=None):
+    """Whole path (prepass + mainloop) in one call; returns BF16 [B, N, H, 128]."""
+    return _one_call(q, k, v, sm_scale, out, workspace, None)
+
+
+def attn_fwd_norm_rope(q, k, v, q_weight, k_weight, cos, sin, eps: float = 1e-6, sm_scale: float = None,
+                       out=None, workspace=None):
+    """attn_fwd on RMSNorm + split-half RoPE of Q and K (as quantize_qkv_norm_rope):
+    K is normalised in the prepass, Q in the mainloop prologue."""
+    N = q.shape[1]
+    nr = _NormRope(_f32_desc(q_weight, (HEAD_DIM,), "q_weight"), _f32_desc(k_weight, (HEAD_DIM,), "k_weight"),
+                   _f32_desc(cos, (N, HEAD_DIM // 2), "cos"), _f32_desc(sin, (N, HEAD_DIM // 2), "sin"), eps)
+    return _one_call(q, k, v, sm_scale, out, workspace, nr)
 
 
 def debug_qk_s32(qz: Quantized):

@@ -381,11 +381,27 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     float qs = 0.0f;
     if (a.q_bf16) {
         // The one-call path quantizes the wave's Q group here, from BF16, with
-        // the prepass's own group routine: identical codes and scale.
+        // the prepass's own group routine: identical codes and scale.  With
+        // the RMSNorm + RoPE producer, the rows are normalised and rotated
+        // first by the prepass's own row routine.
         const int nq = g * kQG + (lane & 31);
+        const bool valid = active && nq < a.N;
         const uint16_t* qp = a.q_bf16 + b * a.q_sb + (int64_t)nq * a.q_sn + h * a.q_sh + 16 * (lane >> 5);
         uint4 codes[4];
-        qs = quant_q_group(qp, active && nq < a.N, codes);
+        if (a.nr.q_weight) {
+            uint4 w[8];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                w[2 * kk] = valid ? *(const uint4*)(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+                w[2 * kk + 1] = valid ? *(const uint4*)(qp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+            }
+            const int na = valid ? nq : 0;
+            norm_rope_row(w, lane >> 5, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2),
+                          a.nr.sin + (int64_t)na * (kHD / 2), a.nr.eps);
+            qs = quant_q_words(w, codes);
+        } else {
+            qs = quant_q_group(qp, valid, codes);
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             qf[kk] = v4i{(int)codes[kk].x, (int)codes[kk].y, (int)codes[kk].z, (int)codes[kk].w};

@@ -156,7 +156,7 @@ sage_status prepass(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf1
 
 // The mainloop over range *r; q_src non-null makes it quantize Q from BF16.
 sage_status mainloop(const sage_quantized* qz, float sm_scale, const sage_range* r, const sage_bf16_out* o,
-                     const sage_bf16_in* q_src, void* stream) {
+                     const sage_bf16_in* q_src, const sage_norm_rope* nr, void* stream) {
     Dims d;
     sage_status st;
     if ((st = check_quantized(qz, &d)) != SAGE_OK) return st;
@@ -177,6 +177,8 @@ sage_status mainloop(const sage_quantized* qz, float sm_scale, const sage_range*
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.q_bf16 = q_src ? (const uint16_t*)q_src->data : nullptr;
     p.q_sb = q_src ? q_src->stride_b : 0; p.q_sn = q_src ? q_src->stride_n : 0; p.q_sh = q_src ? q_src->stride_h : 0;
+    p.nr = sage::NormRopeArgs{nullptr, nullptr, nullptr, nullptr, 0.0f};
+    if (q_src && nr) p.nr = sage::NormRopeArgs{nr->q_weight, nr->k_weight, nr->cos, nr->sin, nr->eps};
     p.o = (uint16_t*)o->data; p.o_sb = o->stride_b; p.o_sn = o->stride_n; p.o_sh = o->stride_h;
     p.B = (int)d.B; p.N = (int)d.N; p.H = (int)d.H; p.T = (int)d.T; p.G = (int)d.G;
     p.q_start = r->q_start;
@@ -192,6 +194,24 @@ sage_status mainloop(const sage_quantized* qz, float sm_scale, const sage_range*
     const float log2e = 1.4426950408889634f;
     p.c = sm_scale * log2e;
     return hip_status(sage::launch_mainloop(p, (hipStream_t)stream), "mainloop launch");
+}
+
+// The whole path in one call; nr non-null adds the RMSNorm + RoPE producer
+// (K in the prepass, Q in the mainloop prologue).
+sage_status one_call(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v, sage_shape s,
+                     const sage_norm_rope* nr, float sm_scale, const sage_bf16_out* o, void* ws, size_t ws_bytes,
+                     void* stream) {
+    sage_quantized qz;
+    sage_status st = sage_quantized_carve(s, ws, ws_bytes, &qz);
+    if (st != SAGE_OK) return st;
+    if ((st = check_out(o)) != SAGE_OK) return st;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+    if ((st = check_in(q, "q")) != SAGE_OK) return st;
+    // K and V through the prepass; Q is quantized inside the mainloop.
+    if ((st = prepass(q, k, v, &qz, false, nr, stream)) != SAGE_OK) return st;
+    const sage_range all = {0, s.N, 0, s.H};
+    return mainloop(&qz, sm_scale, &all, o, q, nr, stream);
 }
 
 }  // namespace
@@ -269,7 +289,7 @@ sage_status sage_quantize_qkv_norm_rope(const sage_bf16_in* q, const sage_bf16_i
 sage_status sage_attn_fwd_quantized_range(const sage_quantized* qz, float sm_scale, const sage_range* r,
                                           const sage_bf16_out* o, void* stream) {
     clear_err();
-    return mainloop(qz, sm_scale, r, o, nullptr, stream);
+    return mainloop(qz, sm_scale, r, o, nullptr, nullptr, stream);
 }
 
 sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, const sage_bf16_out* o,
@@ -285,17 +305,16 @@ sage_status sage_attn_fwd_quantized(const sage_quantized* qz, float sm_scale, co
 sage_status sage_attn_fwd(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v, sage_shape s,
                           float sm_scale, const sage_bf16_out* o, void* ws, size_t ws_bytes, void* stream) {
     clear_err();
-    sage_quantized qz;
-    sage_status st = sage_quantized_carve(s, ws, ws_bytes, &qz);
-    if (st != SAGE_OK) return st;
-    if ((st = check_out(o)) != SAGE_OK) return st;
-    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
-        return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
-    if ((st = check_in(q, "q")) != SAGE_OK) return st;
-    // K and V through the prepass; Q is quantized inside the mainloop.
-    if ((st = prepass(q, k, v, &qz, false, nullptr, stream)) != SAGE_OK) return st;
-    const sage_range all = {0, s.N, 0, s.H};
-    return mainloop(&qz, sm_scale, &all, o, q, stream);
+    return one_call(q, k, v, s, nullptr, sm_scale, o, ws, ws_bytes, stream);
+}
+
+sage_status sage_attn_fwd_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                    sage_shape s, const sage_norm_rope* nr, float sm_scale, const sage_bf16_out* o,
+                                    void* ws, size_t ws_bytes, void* stream) {
+    clear_err();
+    sage_status st;
+    if ((st = check_norm_rope(nr)) != SAGE_OK) return st;
+    return one_call(q, k, v, s, nr, sm_scale, o, ws, ws_bytes, stream);
 }
 
 sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* stream) {

@@ -71,6 +71,7 @@ struct MainloopArgs {
     const int8_t* k_i8; const float* k_scale;
     const uint8_t* v_fp8; const float* v_scale;
     const uint16_t* q_bf16; int64_t q_sb, q_sn, q_sh;  // non-null: quantize Q from BF16 here
+    NormRopeArgs nr;     // nr.q_weight non-null: RMSNorm + RoPE the BF16 Q rows first
     uint16_t* o; int64_t o_sb, o_sn, o_sh;   // output view of the range
     int B, N, H, T, G;
     int q_start, q_end;  // query rows [q_start, q_end) are written

@@ -194,6 +194,16 @@ def test_norm_rope_validation_happens_before_launch(sage):
     bad_shape = _carved(sage)
     bad_shape.shape.D = 64
     assert lib.sage_quantize_qkv_norm_rope(B(good), B(good), B(good), B(ok), B(bad_shape), None) == 1
+    # the one-call form checks the same descriptor, then the workspace
+    shape = sage._Shape(1, 200, 2, 128)
+    need = lib.sage_workspace_bytes(shape)
+    out = sage._Out(0x7d0000000000, 200 * 256, 256, 128)
+    assert lib.sage_attn_fwd_norm_rope(B(good), B(good), B(good), shape, None, ctypes.c_float(0.088), B(out),
+                                       0x7c0000000000, need, None) == 1
+    assert lib.sage_attn_fwd_norm_rope(B(good), B(good), B(good), shape, B(sage._NormRope(w, w, c, s, 0.0)),
+                                       ctypes.c_float(0.088), B(out), 0x7c0000000000, need, None) == 1
+    assert lib.sage_attn_fwd_norm_rope(B(good), B(good), B(good), shape, B(ok), ctypes.c_float(0.088), B(out),
+                                       0x7c0000000000, need - 256, None) == 3
 
 
 def test_error_messages_are_per_thread(sage):

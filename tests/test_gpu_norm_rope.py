@@ -128,3 +128,18 @@ def test_norm_rope_attention_parity(sage, name):
     cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
     _log("  rows=%d max_abs=%.3g cos=%.7f" % (len(rows), max_abs, cos))
     assert max_abs <= MAX_ABS and cos >= MIN_COS
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep_n129", "mid", "canonical"])
+def test_one_call_norm_rope_equals_two_call(sage, name):
+    """sage_attn_fwd_norm_rope (Q normalised, rotated and quantized in the
+    mainloop prologue) writes the same bytes as quantize_qkv_norm_rope +
+    attn_fwd_quantized."""
+    _log("norm_rope one-call vs two-call: %s" % name)
+    w, inp, p, ref = _case(name)
+    q, k, v = _to_gpu(inp)
+    nrp = (p.q_weight.cuda(), p.k_weight.cuda(), p.cos.cuda(), p.sin.cuda())
+    one = sage.attn_fwd_norm_rope(q, k, v, *nrp, p.eps)
+    two = sage.attn_fwd_quantized(sage.quantize_qkv_norm_rope(q, k, v, *nrp, p.eps))
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
