@@ -43,7 +43,8 @@
 extern "C" {
 #endif
 
-#define SAGE_ABI_VERSION 1
+/* 2: adds sage_quantize_qkv_norm_rope and sage_attn_fwd_norm_rope (additions only). */
+#define SAGE_ABI_VERSION 2
 #define SAGE_HEAD_DIM 128
 
 typedef enum sage_status {

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(sage):
     lib = ctypes.CDLL(sage.library_path())
     missing = [n for n in _declared_functions() if not hasattr(lib, n)]
     assert missing == []
-    assert sage._load().sage_abi_version() == 1
+    assert sage._load().sage_abi_version() == 2
 
 
 def test_workspace_bytes(sage):
