@@ -7,7 +7,8 @@
 // Architecture Decision", "Non-Negotiable Dataflow": the exact global K mean
 // and V-scale prepasses are kept.
 //
-// Every kernel here is HBM-bound.  The arithmetic is FP32 with no contraction
+// Every kernel here streams HBM (the RMSNorm + RoPE variants add about a
+// thousand vector instructions per row pair).  The arithmetic is FP32 with no contraction
 // (the library is built with -ffp-contract=off), in the order the C-ABI header
 // states, so the outputs are bit-identical to a plain sequential evaluation.
 //
