@@ -198,6 +198,37 @@ def test_attention_parity_sampled_rows(sage, name, per_head):
     _attn_check(sage, name, rows=_sample_rows(w, per_head, seed=7))
 
 
+def test_attention_parity_canonical_whole_q_blocks(sage):
+    """The launches bench.py times (sage_quantize_qkv + sage_attn_fwd_quantized)
+    on the full long-context shape, against the oracle on 16 whole 128-row Q
+    blocks of every head: block 0, block 295 (the ragged one, 50 rows) and 14
+    seeded random blocks, about 110,000 rows."""
+    import oracle
+    name = "canonical"
+    w = workloads.by_name(name)
+    q, k, v = _to_gpu(_cpu_inputs(name))
+    out = sage.attn_fwd_quantized(sage.quantize_qkv(q, k, v))
+    torch.cuda.synchronize()
+    nblk = -(-w.N // 128)
+    rng = np.random.default_rng(11)
+    rows = []
+    for h in range(w.H):
+        blocks = {0, nblk - 1} | set(rng.choice(np.arange(1, nblk - 1), 14, replace=False).tolist())
+        for qb in sorted(blocks):
+            rows += [(0, h, r) for r in range(128 * qb, min(128 * qb + 128, w.N))]
+    rows = np.array(rows, np.int64)
+    _log("attn canonical whole Q blocks: %d rows" % len(rows))
+    ref_bits, _ = oracle.attn_rows(_oracle_quant(name), rows)
+    got_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got = _dec_bf16(got_bits).astype(np.float64)
+    ref = _dec_bf16(ref_bits).astype(np.float64)
+    max_abs = float(np.max(np.abs(got - ref)))
+    cos = _cos(got, ref)
+    exact = float(np.mean(got_bits == ref_bits))
+    _log("  max_abs=%.3g cos=%.7f bit-equal=%.3f" % (max_abs, cos, exact))
+    assert max_abs <= MAX_ABS and cos >= MIN_COS and exact >= MIN_BIT_EQUAL
+
+
 @pytest.mark.parametrize("sm_scale", [0.02, 0.3, 3.0])
 def test_attention_parity_other_scales(sage, sm_scale):
     """Score scales from well below to well above the canonical one (3.0 makes
