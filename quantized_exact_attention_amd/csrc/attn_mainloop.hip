@@ -12,8 +12,9 @@
 // gfx950 design (not the pages' GB10 one):
 //   * A workgroup of kMainloopWaves (4) wavefronts owns 128 query rows of one
 //     (b, h); wave w owns the 32-row group g = 4*qb + w, so its Q scale is
-//     wave-uniform.  Two workgroups share a CU (two waves per SIMD) and
-//     synchronise independently of each other.
+//     wave-uniform.  Three workgroups share a CU (three waves per SIMD, at
+//     most 168 VGPRs each) and synchronise independently of each other, so
+//     one wave's vector work overlaps the other waves' matrix instructions.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8: lane l then holds 32 keys of the single query
 //     row l%32 (lanes l and l^32 share a row), so the row max and sum are
@@ -23,8 +24,8 @@
 //     scales 1.0), accumulating straight into the FP32 RO rows after the alpha
 //     rescale, tile by tile in increasing order.
 //   * K and V tiles (8 KiB each, already in operand order) stream through
-//     LDS rings filled by direct global-to-LDS loads issued two to three
-//     tiles ahead of their use.
+//     three-slot LDS rings (48 KiB per workgroup) filled by direct
+//     global-to-LDS loads issued two tiles ahead of their use.
 //   * The workgroup-to-(b, h, Q block) map keeps the workgroups that one XCD
 //     runs on the same head, so that head's K/V stream is shared in its L2.
 #include "sage_device.hpp"
@@ -80,9 +81,13 @@ __device__ __forceinline__ int key_of(int blk, int r, int lane) {
     return 32 * blk + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// E4M3 x E4M3 -> FP32, 32x32x64, both block scales 1.0 (E8M0 127).
+// E4M3 x E4M3 -> FP32, 32x32x64 without block scales: zero scale operands
+// select the unscaled v_mfma_f32_32x32x64_f8f6f4 (same products as unit
+// scales).  The unscaled form also has no scale VGPR operand, whose value
+// the scaled form reads with a latency that a write a few instructions
+// earlier does not meet.
 __device__ __forceinline__ v16f mfma_pv(const v8i& vf, const v8i& pk, const v16f& acc) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, acc, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pk, acc, 0, 0, 0, 0, 0, 0);
 }
 
 // PV of one wave against one staged V tile: ro[db] += V^T(rows 32db..) . P^T,
@@ -164,17 +169,17 @@ __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
         for (int r = 0; r < 16; ++r) ro[db][r] *= alpha;
 }
 
-// LDS rings: K tiles in 3 slots, V tiles in 4 slots, filled straight from
-// global memory by global_load_lds_dwordx4 (no VGPR staging).  In iteration j
-// a wave issues PV of tile j-1, the softmax of tile j (scores computed in the
-// previous iteration) and QK of tile j+1, while the workgroup's loads of
-// K(j+3) and V(j+2) are in flight; the loads issued one iteration earlier are
-// waited for before the barrier that ends the iteration.  The slots change
-// roles by pointer rotation, not by index arithmetic.  RO receives every
-// tile's PV in increasing tile order, each after the rescale by that tile's
-// alpha.
+// LDS rings: K and V tiles in 3 slots each, filled straight from global
+// memory by global_load_lds_dwordx4 (no VGPR staging).  In iteration j a
+// wave runs the softmax of tile j (scores computed in the previous
+// iteration), the PV of tile j and the QK of tile j+1, while the workgroup's
+// loads of K(j+3) and V(j+2) are in flight; the loads issued one iteration
+// earlier are waited for before the barrier that ends the iteration.  The
+// slots change roles by pointer rotation, not by index arithmetic.  RO
+// receives every tile's PV in increasing tile order, each after the rescale
+// by that tile's alpha.
 constexpr int kKSlots = 3;
-constexpr int kVSlots = 4;
+constexpr int kVSlots = 3;
 
 // Each wave copies its share (kTileLoads KiB) of an 8 KiB tile from global
 // memory into an LDS slot; lane l's 16 bytes of each KiB land at that KiB's
@@ -226,141 +231,7 @@ typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
 #define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Operand reads from a staged tile; `lane_base` is the slot address plus
-// 16*lane, so every read of an iteration is one base register plus an
-// immediate offset.
-__device__ __forceinline__ v8i load_vfrag(const int8_t* lane_base, int db) {
-    const v4i lo = *(const v4i*)(lane_base + (db * 2 + 0) * 1024);
-    const v4i hi = *(const v4i*)(lane_base + (db * 2 + 1) * 1024);
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-__device__ __forceinline__ v4i load_kfrag(const int8_t* lane_base, int blk, int kk) {
-    return *(const v4i*)(lane_base + (blk * 4 + kk) * 1024);
-}
-
-
-__device__ __forceinline__ v16i mfma_qk(const v4i& kf, const v4i& qf, const v16i& acc) {
-    return __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf, acc, 0, 0, 0);
-}
-
-// One steady-state iteration for tile j (not the last): PV of tile j-1, the
-// softmax of tile j and QK of tile j+1, written as a fixed sequence in which
-// each matrix instruction is followed by a slice of the softmax's vector
-// work (fenced so the compiler keeps the order), and each LDS operand read
-// is issued at least one step before its use (the first two V operands of
-// the next iteration at the end of this one, in va/vb).  One wavefront
-// thereby keeps its matrix and vector pipes busy together.  `bias` holds
-// kScoreBias in every register, the initial QK accumulator.  Numerically
-// identical to softmax_tile followed by pv_tile / qk_tile.
-__device__ __forceinline__ void steady_iteration(const int8_t* vtile_prev, const int8_t* ktile_next,
-                                                 const int8_t* vtile_after, v8i& va, v8i& vb,
-                                                 const v4i (&qf)[4], int lane, float sj, float& m, float& dpart,
-                                                 float& alpha, v8i& pk, v16i& s0, v16i& s1, v16f (&ro)[4],
-                                                 const v16i& bias) {
-    const v8i pprev = pk;
-    const int8_t* vbase = vtile_prev + lane * 16;
-    const int8_t* kbase = ktile_next + lane * 16;
-    v8i vf0 = load_vfrag(vbase, 2);
-    v8i vf1 = load_vfrag(vbase, 3);
-    ro[0] = mfma_pv(va, pprev, ro[0]);
-    SAGE_FENCE();
-    int ma = max(s0[0], s0[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) ma = max(max(ma, s0[r]), s0[r + 1]);
-    ro[1] = mfma_pv(vb, pprev, ro[1]);
-    SAGE_FENCE();
-    int mb = max(s1[0], s1[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mb = max(max(mb, s1[r]), s1[r + 1]);
-    const int mx = halves_max(max(ma, mb)) - kScoreBias;
-    const float m_new = fmaxf(m, (float)mx * sj);
-    alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    const float off = kLog2Of448 - m_new;
-    ro[2] = mfma_pv(vf0, pprev, ro[2]);
-    SAGE_FENCE();
-    float x[32];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = __builtin_fmaf(unbias(s0[r]), sj, off);
-    v4i ka = load_kfrag(kbase, 0, 0);
-    v4i kb = load_kfrag(kbase, 1, 0);
-    ro[3] = mfma_pv(vf1, pprev, ro[3]);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 8; r < 16; ++r) x[r] = __builtin_fmaf(unbias(s0[r]), sj, off);
-    v16i n0 = mfma_qk(ka, qf[0], bias);
-    ka = load_kfrag(kbase, 0, 1);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 0; r < 8; ++r) x[16 + r] = __builtin_fmaf(unbias(s1[r]), sj, off);
-    v16i n1 = mfma_qk(kb, qf[0], bias);
-    kb = load_kfrag(kbase, 1, 1);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 8; r < 16; ++r) x[16 + r] = __builtin_fmaf(unbias(s1[r]), sj, off);
-    n0 = mfma_qk(ka, qf[1], n0);
-    ka = load_kfrag(kbase, 0, 2);
-    SAGE_FENCE();
-    float p[32];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
-    n1 = mfma_qk(kb, qf[1], n1);
-    kb = load_kfrag(kbase, 1, 2);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 8; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
-    n0 = mfma_qk(ka, qf[2], n0);
-    ka = load_kfrag(kbase, 0, 3);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 16; r < 24; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
-    n1 = mfma_qk(kb, qf[2], n1);
-    kb = load_kfrag(kbase, 1, 3);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 24; r < 32; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
-    n0 = mfma_qk(ka, qf[3], n0);
-    SAGE_FENCE();
-    float d0 = dpart * alpha, d1 = p[1], d2 = p[2], d3 = p[3];
-    d0 += p[0];
-#pragma unroll
-    for (int r = 4; r < 16; r += 4) {
-        d0 += p[r];
-        d1 += p[r + 1];
-        d2 += p[r + 2];
-        d3 += p[r + 3];
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], __float_as_int(p[4 * v]));
-        pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
-    }
-    n1 = mfma_qk(kb, qf[3], n1);
-    // first two V operands of the next iteration's PV (that tile is already
-    // published), so its first matrix instructions do not wait on LDS
-    const int8_t* vnext = vtile_after + lane * 16;
-    va = load_vfrag(vnext, 0);
-    vb = load_vfrag(vnext, 1);
-    SAGE_FENCE();
-#pragma unroll
-    for (int r = 16; r < 32; r += 4) {
-        d0 += p[r];
-        d1 += p[r + 1];
-        d2 += p[r + 2];
-        d3 += p[r + 3];
-    }
-    dpart = (d0 + d1) + (d2 + d3);
-#pragma unroll
-    for (int v = 4; v < 8; ++v) {
-        const int w = cvt_pk_e4m3<false>(p[4 * v], p[4 * v + 1], __float_as_int(p[4 * v]));
-        pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
-    }
-    s0 = n0;
-    s1 = n1;
-}
-
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(MainloopArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void mainloop_kernel(MainloopArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
     __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
 
@@ -375,7 +246,6 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     const int g = a.g_begin + qb * kWaves + wave;
     const bool active = g < a.g_end && g * kQG < a.N;
     const int T = a.T;
-    const int tid16 = threadIdx.x * 16;
 
     v4i qf[4];
     float qs = 0.0f;
@@ -420,17 +290,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     const const_f32_ptr ksc = (const_f32_ptr)(a.k_scale + (int64_t)bh * T);
     const float c = a.c;
 
-    // Prologue: K(0..2) and V(0..1) in flight to LDS; V slot 3 zeroed so the
-    // PV of "tile -1" in iteration 0 adds exact zeros.  Loads past the last
-    // tile are clamped to it and land in slots that are never read again.
+    // Prologue: K(0..2) and V(0..1) to LDS, then QK of tile 0.  Loads past
+    // the last tile are clamped to it and land in slots that are never read
+    // again.
     tile_to_lds(kg, lds_k, wave, lane);
     tile_to_lds(vg, lds_v, wave, lane);
     tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, wave, lane);
     tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, wave, lane);
     tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, wave, lane);
-    #pragma unroll
-    for (int i = 0; i < kTileLoads; ++i)
-        *(v4i*)(lds_v + 3 * kTileBytes + i * kThreads * 16 + tid16) = v4i{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     v16i s0, s1;
@@ -444,57 +311,59 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void mainloop_kernel(Mainloop
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ro[db][r] = 0.0f;
-    v8i pprev = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-
-    // alpha of the previous tile, applied to RO just before that tile's PV
-    float alpha_prev = 1.0f;
-    bool pending = false;
-    // kept in registers for the whole loop (the empty asm hides the constant
-    // from the compiler, which would otherwise rebuild it every iteration)
+    // the initial QK accumulator, kept in registers for the whole loop (the
+    // empty asm hides the constant from the compiler, which would otherwise
+    // rebuild it every iteration)
     v16i bias = v16i{kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
                      kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
                      kScoreBias, kScoreBias};
     asm volatile("" : "+v"(bias));
     // Ring slots by role, rotated each iteration: kq holds K(j+1) for this
-    // iteration's QK and kf receives K(j+3); vp holds V(j-1) for this
-    // iteration's PV and vf receives V(j+2).
+    // iteration's QK, kn K(j+2), and kf receives K(j+3); vc holds V(j) for
+    // this iteration's PV, vn V(j+1), and vf receives V(j+2).
     int8_t* kq = lds_k + kTileBytes;
     int8_t* kn = lds_k + 2 * kTileBytes;
     int8_t* kf = lds_k;
-    int8_t* vp = lds_v + 3 * kTileBytes;
-    int8_t* v0 = lds_v;
-    int8_t* v1 = lds_v + kTileBytes;
+    int8_t* vc = lds_v;
+    int8_t* vn = lds_v + kTileBytes;
     int8_t* vf = lds_v + 2 * kTileBytes;
-    v8i va = load_vfrag(vp + lane * 16, 0);
-    v8i vb = load_vfrag(vp + lane * 16, 1);
-    float ksj = ksc[0];    // K scales are read one tile ahead
     for (int j = 0; j < T - 1; ++j) {
-        const float ksj_next = ksc[min(j + 1, T - 1)];
         tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, wave, lane);
         tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, wave, lane);
         if (active) {
-            if (pending) rescale(ro, alpha_prev);
-            steady_iteration(vp, kq, v0, va, vb, qf, lane, (qs * ksj) * c, m, dpart, alpha_prev, pprev, s0, s1, ro, bias);
-            pending = __any(alpha_prev != 1.0f);
+            // softmax of tile j, the alpha rescale of RO (skipped when no row
+            // of the wave changed its max), PV of tile j, QK of tile j+1
+            float alpha;
+            v8i pk;
+            softmax_tile<false>(s0, s1, (qs * ksc[j]) * c, 0, lane, m, dpart, alpha, pk);
+            if (__any(alpha != 1.0f)) rescale(ro, alpha);
+            SAGE_FENCE();
+            pv_tile(vc, pk, lane, ro);
+            s0 = bias;
+            s1 = bias;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i a0 = *(const v4i*)(kq + ((0 * 4 + kk) * 64 + lane) * 16);
+                const v4i a1 = *(const v4i*)(kq + ((1 * 4 + kk) * 64 + lane) * 16);
+                s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qf[kk], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qf[kk], s1, 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
         block_barrier();
         int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
-        t = vp;  vp = v0;  v0 = v1;  v1 = vf;  vf = t;
-        ksj = ksj_next;
+        t = vf;  vf = vc;  vc = vn;  vn = t;
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     if (!active) return;
     {
         const int j = T - 1;
-        if (pending) rescale(ro, alpha_prev);
-        pv_tile(vp, pprev, lane, ro);                // V(T-2), or zeros when T == 1
         float alpha;
         v8i pk;
         softmax_tile<true>(s0, s1, (qs * ksc[j]) * c, a.N - j * kBK, lane, m, dpart, alpha, pk);
         if (__any(alpha != 1.0f)) rescale(ro, alpha);
-        pv_tile(v0, pk, lane, ro);                   // V(T-1)
+        pv_tile(vc, pk, lane, ro);                   // V(T-1)
     }
 
     const float dtot = halves_sum(dpart);
