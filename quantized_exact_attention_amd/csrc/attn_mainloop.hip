@@ -20,9 +20,12 @@
 //     row l%32 (lanes l and l^32 share a row), so the row max and sum are
 //     in-lane plus one exchange with lane l^32, and the FP8 probabilities
 //     are already in the B-operand layout of the PV instruction.
-//   * PV is O^T = V^T . P^T with v_mfma_scale_f32_32x32x64_f8f6f4 (block
-//     scales 1.0), accumulating straight into the FP32 RO rows after the alpha
-//     rescale, tile by tile in increasing order.
+//   * PV is O^T = V^T . P^T with the unscaled v_mfma_f32_32x32x64_f8f6f4,
+//     accumulating straight into the FP32 RO rows after the alpha rescale,
+//     tile by tile in increasing order.
+//   * Per iteration a wave runs a vector phase (the softmax of one tile) and
+//     then a matrix phase (that tile's PV and the next tile's QK); the three
+//     waves of a SIMD overlap each other's phases.
 //   * K and V tiles (8 KiB each, already in operand order) stream through
 //     three-slot LDS rings (48 KiB per workgroup) filled by direct
 //     global-to-LDS loads issued two tiles ahead of their use.
@@ -36,6 +39,9 @@ namespace {
 
 constexpr int kWaves = kMainloopWaves;
 constexpr int kThreads = kWaves * 64;
+// Workgroups per CU = waves per SIMD: the register budget (512 / 3 -> 168
+// VGPRs per wave) the compiler is held to, and 3 x 48 KiB of LDS.
+constexpr int kWavesPerSimd = 3;
 // 1 KiB DMA instructions per wave per 8 KiB tile
 constexpr int kTileLoads = kTileBytes / (kWaves * 1024);
 static_assert(kTileLoads * kWaves * 1024 == kTileBytes, "tile split");
@@ -231,7 +237,7 @@ typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
 #define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-__global__ __launch_bounds__(kThreads, 3) void mainloop_kernel(MainloopArgs a) {
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(MainloopArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
     __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
 

@@ -2,7 +2,7 @@
 //
 // Operand layouts of the two matrix instructions the mainloop uses (measured
 // on gfx950 and fixed by the library's byte layouts):
-//   v_mfma_i32_32x32x32_i8 and v_mfma_scale_f32_32x32x64_f8f6f4:
+//   v_mfma_i32_32x32x32_i8 and v_mfma_(scale_)f32_32x32x64_f8f6f4:
 //     A: lane l holds row l%32, k-bytes [K/2 * (l/32), K/2 * (l/32) + K/2)
 //     B: lane l holds column l%32, the same k-bytes
 //     C/D: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
