@@ -191,25 +191,27 @@ constexpr int kVSlots = 3;
 // memory into an LDS slot; lane l's 16 bytes of each KiB land at that KiB's
 // base + 16*l (LDS address taken from M0, which is restored afterwards; the
 // instruction reads it at issue, one wait state after the SALU write).
+// The global address is the tile base in an SGPR pair (wave-uniform, formed
+// by scalar instructions) plus the lane's fixed 32-bit byte offset `voff`
+// (+1 KiB per further load), so the loads cost no vector instructions.
 // Issued as inline assembly so that the compiler does not make every later
 // LDS read wait for these loads: the instruction writes no
 // VGPR, and the only consumer synchronisation is the explicit vmcnt wait
 // before the block barrier that publishes the tile.
-__device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, int wave, int lane) {
+__device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, uint32_t voff, int wave) {
 #pragma unroll
     for (int i = 0; i < kTileLoads; ++i) {
         const int part = wave * kTileLoads + i;
-        const int8_t* src = gtile + (part * 64 + lane) * 16;
         const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(slot + part * 1024));
         uint32_t saved_m0;
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %2\n\t"
+            "s_mov_b32 m0, %3\n\t"
             "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %1, off\n\t"
+            "global_load_lds_dwordx4 %1, %2\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved_m0)
-            : "v"(src), "s"(dst)
+            : "v"(voff + i * 1024), "s"(gtile), "s"(dst)
             : "memory");
     }
 }
@@ -249,6 +251,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     const int bh = b * a.H + h;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
+    // this lane's byte offset in a tile for its first 1 KiB tile load
+    const uint32_t voff = (uint32_t)((wave * kTileLoads * 64 + lane) * 16);
     const int g = a.g_begin + qb * kWaves + wave;
     const bool active = g < a.g_end && g * kQG < a.N;
     const int T = a.T;
@@ -299,11 +303,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     // Prologue: K(0..2) and V(0..1) to LDS, then QK of tile 0.  Loads past
     // the last tile are clamped to it and land in slots that are never read
     // again.
-    tile_to_lds(kg, lds_k, wave, lane);
-    tile_to_lds(vg, lds_v, wave, lane);
-    tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, wave, lane);
-    tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, wave, lane);
-    tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, wave, lane);
+    tile_to_lds(kg, lds_k, voff, wave);
+    tile_to_lds(vg, lds_v, voff, wave);
+    tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, voff, wave);
+    tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, voff, wave);
+    tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, voff, wave);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     v16i s0, s1;
@@ -334,8 +338,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     int8_t* vn = lds_v + kTileBytes;
     int8_t* vf = lds_v + 2 * kTileBytes;
     for (int j = 0; j < T - 1; ++j) {
-        tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, wave, lane);
-        tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, wave, lane);
+        tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, voff, wave);
+        tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, voff, wave);
         if (active) {
             // softmax of tile j, the alpha rescale of RO (skipped when no row
             // of the wave changed its max), PV of tile j, QK of tile j+1
