@@ -111,14 +111,27 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
 // Online softmax of one tile for this lane's query row (32 of the tile's keys
 // here, the other 32 on lane l^32), on biased sums (kScoreBias): max update on
 // the exact int32 sums (the score scale sj is positive, so the largest sum
-// gives the largest score), alpha = 2^(m - m_new), p = 448 * 2^(t - m_new)
-// with 448 folded into the exponent offset, this lane's part of the
-// denominator, and the FP8 codes packed in the B-operand order of the PV
-// instruction.  kLast masks keys at or beyond `tail` in the final, partial
-// tile.
+// gives the largest score), alpha = 2^(m - m_new), p = 448 * 2^(t - m_new),
+// this lane's part of the denominator, and the FP8 codes packed in the
+// B-operand order of the PV instruction.  kLast masks keys at or beyond
+// `tail` in the final, partial tile.
+//
+// p = 2^fma(S, sj, off) with 448 folded into off = log2(448) - m.  off is
+// kept across tiles and recomputed only when some row maximum of the wave
+// moves; `moved` reports that, which is also exactly when RO needs the alpha
+// rescale.  For the largest score the exponent is log2(448) plus the rounding
+// errors of m and of off, about one unit in the last place of m together.
+// That is negligible for the maxima of real attention (|m| below 2^5 in log2
+// units in the pages' workloads); from |m| = 2^17 on it reaches 2^-6 and the
+// outputs move visibly away from those of the stepwise rounding; from
+// |m| = 2^20 on it can lift the largest p past 464, which converts to NaN.
+// There off is lowered by two units in the last place of m, which keeps every
+// p at or below 448.
+constexpr float kOffsetGuardFrom = 1048576.0f;   // 2^20
+
 template <bool kLast>
 __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int tail, int lane, float& m,
-                                             float& dpart, float& alpha, v8i& pk) {
+                                             float& off, float& dpart, float& alpha, bool& moved, v8i& pk) {
     if (kLast) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -136,8 +149,16 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
     const int mx = halves_max(max(ma, mb)) - kScoreBias;
     const float m_new = fmaxf(m, (float)mx * sj);
     alpha = __builtin_amdgcn_exp2f(m - m_new);
+    moved = __any(m_new != m);
+    if (moved) {
+        off = kLog2Of448 - m_new;
+        if (!(__builtin_fabsf(m_new) < kOffsetGuardFrom)) {
+            // two units in the last place of m (|m| >= 2^20 is a normal number)
+            const float u2 = __int_as_float((__float_as_int(m_new) & 0x7F800000) - (22 << 23));
+            off -= u2;
+        }
+    }
     m = m_new;
-    const float off = kLog2Of448 - m_new;
     float p[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -315,6 +336,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     __syncthreads();   // K slot 0 is refilled in iteration 0
 
     float m = -INFINITY;
+    float off = 0.0f;      // log2(448) - m, set when m first moves
     float dpart = 0.0f;    // this lane's share of the row denominator
     v16f ro[4];
 #pragma unroll
@@ -345,8 +367,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
             // of the wave changed its max), PV of tile j, QK of tile j+1
             float alpha;
             v8i pk;
-            softmax_tile<false>(s0, s1, (qs * ksc[j]) * c, 0, lane, m, dpart, alpha, pk);
-            if (__any(alpha != 1.0f)) rescale(ro, alpha);
+            bool moved;
+            softmax_tile<false>(s0, s1, (qs * ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
+            if (moved) rescale(ro, alpha);
             SAGE_FENCE();
             pv_tile(vc, pk, lane, ro);
             s0 = bias;
@@ -371,8 +394,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
         const int j = T - 1;
         float alpha;
         v8i pk;
-        softmax_tile<true>(s0, s1, (qs * ksc[j]) * c, a.N - j * kBK, lane, m, dpart, alpha, pk);
-        if (__any(alpha != 1.0f)) rescale(ro, alpha);
+        bool moved;
+        softmax_tile<true>(s0, s1, (qs * ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha, moved, pk);
+        if (moved) rescale(ro, alpha);
         pv_tile(vc, pk, lane, ro);                   // V(T-1)
     }
 
