@@ -148,9 +148,11 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
     }
     const int mx = halves_max(max(ma, mb)) - kScoreBias;
     const float m_new = fmaxf(m, (float)mx * sj);
-    alpha = __builtin_amdgcn_exp2f(m - m_new);
     moved = __any(m_new != m);
+    alpha = 1.0f;           // 2^(m - m_new) is exactly 1 where m does not move
     if (moved) {
+        alpha = __builtin_amdgcn_exp2f(m - m_new);
+        dpart *= alpha;
         off = kLog2Of448 - m_new;
         if (!(__builtin_fabsf(m_new) < kOffsetGuardFrom)) {
             // two units in the last place of m (|m| >= 2^20 is a normal number)
@@ -172,7 +174,7 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
             if (key_of(1, r, lane) >= tail) p[16 + r] = 0.0f;
         }
     }
-    float d0 = dpart * alpha, d1 = p[1], d2 = p[2], d3 = p[3];
+    float d0 = dpart, d1 = p[1], d2 = p[2], d3 = p[3];
     d0 += p[0];
 #pragma unroll
     for (int r = 4; r < 32; r += 4) {
