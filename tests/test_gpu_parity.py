@@ -103,6 +103,42 @@ def test_cvt_e4m3_matches_oracle(sage):
     assert bad.size == 0, [(float(x[i]), int(got[i]), int(ref[i])) for i in bad[:5]]
 
 
+def test_cvt_e4m3_exhaustive_in_range(sage):
+    """Every FP32 bit pattern with |x| <= 464 (about 2.28e9 values, both
+    signs): the kernels' E4M3 conversion equals the oracle's RNE encoder.
+    That range holds every value the kernels convert (V times its inverse
+    scale is at most 448; a probability exceeds 448 by at most a few
+    thousandths of its exponent).  The oracle runs in host threads, one
+    slice of each chunk per thread."""
+    import concurrent.futures
+    import os
+    import oracle
+    top = int(np.array(464.0, np.float32).view(np.uint32))        # 0x43E80000
+    chunk = 1 << 26
+    workers = max(1, min(16, os.cpu_count() or 1))
+    oracle.e4m3_encode(np.zeros(1, np.float32))     # load the library before the threads start
+    bad = 0
+    done = 0
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        for sign in (0, 0x80000000):
+            for start in range(0, top + 1, chunk):
+                stop = min(start + chunk, top + 1)
+                bits = np.arange(start, stop, dtype=np.uint32) | np.uint32(sign)
+                x = bits.view(np.float32)
+                got = sage.debug_cvt_e4m3(torch.from_numpy(x).cuda()).cpu().numpy()
+                cuts = np.linspace(0, x.size, workers + 1).astype(np.int64)
+                refs = list(pool.map(lambda i: oracle.e4m3_encode(x[cuts[i]:cuts[i + 1]]), range(workers)))
+                ref = np.concatenate(refs)
+                mism = np.nonzero(got != ref)[0]
+                if mism.size:
+                    _log("cvt mismatch at x=%r: gpu %#x oracle %#x" % (float(x[mism[0]]), got[mism[0]], ref[mism[0]]))
+                bad += mism.size
+                done += x.size
+    _log("cvt_e4m3 exhaustive: %d values, %d mismatches" % (done, bad))
+    assert done == 2 * (top + 1)
+    assert bad == 0
+
+
 # -------------------------------------------------------- quantized bytes --
 
 @pytest.mark.parametrize("name", ALL)
