@@ -516,3 +516,43 @@ def test_ragged_shape_batch3_sampled_rows(sage):
     assert np.max(np.abs(got - want)) <= MAX_ABS
     assert _cos(got, want) >= MIN_COS
     assert np.mean(got_bits == ref_bits) >= MIN_BIT_EQUAL
+
+
+def test_offsets_beyond_2gib(sage):
+    """B = 1, H = 4100, N = 4096: each input tensor holds 2.15e9 elements
+    (4.3 GB) and the INT8 Q and K regions 2.15 GB each, so the element and
+    byte offsets of the last heads need more than 31 bits.  For heads 0 and
+    4095..4099: every quantized byte, scale and the K mean bit-exact, and
+    sampled output rows of the timed two-call path within the bar, against
+    the oracle run on just those heads (heads are independent)."""
+    import oracle
+    B, N, H = 1, 4096, 4100
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    q = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k += 3.0 * torch.randn((H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    qz = sage.quantize_qkv(q, k, v)
+    out = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    G, T = qz.G, qz.T
+    assert (H - 1) * G * 4096 >= 2 ** 31 and (H - 1) * N * 128 >= 2 ** 31
+    rng = np.random.default_rng(5)
+    for h in [0, 4095, 4096, 4097, 4098, 4099]:
+        qh, kh, vh = (t[:, :, h:h + 1].cpu() for t in (q, k, v))
+        ref = oracle.quantize(qh, kh, vh)
+        assert np.array_equal(_bits(qz.k_mean[0, h].cpu().numpy()), _bits(ref.k_mean.reshape(-1)))
+        assert np.array_equal(_bits(qz.q_scale[0, h].cpu().numpy()), _bits(ref.q_scale.reshape(-1)))
+        assert np.array_equal(_bits(qz.k_scale[0, h].cpu().numpy()), _bits(ref.k_scale.reshape(-1)))
+        assert np.array_equal(_bits(qz.v_scale[0, h].cpu().numpy()), _bits(ref.v_scale.reshape(-1)))
+        gq = layouts.q_logical(qz.q_i8[h * G * 4096:(h + 1) * G * 4096].cpu().numpy(), 1, 1, N)
+        gk = layouts.k_logical(qz.k_i8[h * T * 8192:(h + 1) * T * 8192].cpu().numpy(), 1, 1, N)
+        gv = layouts.v_logical(qz.v_fp8[h * T * 8192:(h + 1) * T * 8192].cpu().numpy(), 1, 1, N)
+        assert np.array_equal(gq, ref.q_i8) and np.array_equal(gk, ref.k_i8) and np.array_equal(gv, ref.v8)
+        rr = sorted({0, 31, 2048, N - 1} | set(rng.choice(N, 20, replace=False).tolist()))
+        ref_bits, _ = oracle.attn_rows(ref, np.array([[0, 0, r] for r in rr], np.int64))
+        got_bits = out[0, rr, h].view(torch.int16).cpu().numpy().view(np.uint16)
+        got = _dec_bf16(got_bits).astype(np.float64)
+        want = _dec_bf16(ref_bits).astype(np.float64)
+        assert np.max(np.abs(got - want)) <= MAX_ABS and _cos(got, want) >= MIN_COS
+    _log("offsets beyond 2 GiB: heads 0, 4095..4099 bit-exact bytes and output rows within the bar")
