@@ -556,3 +556,37 @@ def test_offsets_beyond_2gib(sage):
         want = _dec_bf16(ref_bits).astype(np.float64)
         assert np.max(np.abs(got - want)) <= MAX_ABS and _cos(got, want) >= MIN_COS
     _log("offsets beyond 2 GiB: heads 0, 4095..4099 bit-exact bytes and output rows within the bar")
+
+
+def test_long_sequence_one_head(sage):
+    """N = 2^20 + 37 tokens of one head (16,385 KV tiles, the last with 37
+    keys; 8,192 Q blocks): every quantized byte, scale and the K mean
+    (a 2^20-term mean) bit-exact, and 24 sampled output rows (the first
+    group, the ragged last rows, random rows) of the two-call path within
+    the bar."""
+    import oracle
+    B, N, H = 1, (1 << 20) + 37, 1
+    w = workloads.Workload("long", B, N, H, seed=78)
+    inp = workloads.generate(w)
+    q, k, v = _to_gpu(inp)
+    qz = sage.quantize_qkv(q, k, v)
+    out = sage.attn_fwd_quantized(qz)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(inp.q, inp.k, inp.v)
+    assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
+    assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    assert np.array_equal(layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N), ref.q_i8)
+    assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N), ref.k_i8)
+    assert np.array_equal(layouts.v_logical(qz.v_fp8.cpu().numpy(), B, H, N), ref.v8)
+    rng = np.random.default_rng(9)
+    rr = sorted({0, 31, N - 37, N - 1} | set(rng.choice(N, 20, replace=False).tolist()))
+    rows = np.array([[0, 0, r] for r in rr], np.int64)
+    ref_bits, _ = oracle.attn_rows(ref, rows)
+    got_bits = out[0, rr, 0].view(torch.int16).cpu().numpy().view(np.uint16)
+    got = _dec_bf16(got_bits).astype(np.float64)
+    want = _dec_bf16(ref_bits).astype(np.float64)
+    max_abs, cos = float(np.max(np.abs(got - want))), _cos(got, want)
+    _log("long sequence N=%d: max_abs=%.3g cos=%.7f bit-equal=%.3f" % (N, max_abs, cos, float(np.mean(got_bits == ref_bits))))
+    assert max_abs <= MAX_ABS and cos >= MIN_COS
