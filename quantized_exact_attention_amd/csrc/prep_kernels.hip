@@ -8,9 +8,10 @@
 // and V-scale prepasses are kept.
 //
 // Every kernel here streams HBM (the RMSNorm + RoPE variants add about a
-// thousand vector instructions per row pair).  The arithmetic is FP32 with no contraction
-// (the library is built with -ffp-contract=off), in the order the C-ABI header
-// states, so the outputs are bit-identical to a plain sequential evaluation.
+// thousand vector instructions per row pair).  The arithmetic is FP32 with no
+// contraction (the library is built with -ffp-contract=off), in the order the
+// C-ABI header states, so the outputs are bit-identical to a plain sequential
+// evaluation.
 //
 // Launch sequence (one stream):
 //   1. tile_stats    per 64-row tile: FP32 in-order channel sums of K and
@@ -181,19 +182,6 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     a.v_inv[(int64_t)bh * kHD + d] = inv;
 }
 
-// One block of 256 threads per (b, h, 64-row tile t) quantizes everything the
-// tile's rows hold, so each projection row segment is read once:
-//   waves 0, 1  Q groups 2t and 2t+1 (when Q is quantized here): lane l reads
-//               row 32g + l%32, channels 32kk + 16*(l/32) + 0..15, exactly the
-//               16 bytes it writes for kk
-//   waves 2, 3  K rows 64t + 32*(w-2) + l%32, same channel split; the tile's
-//               absolute maximum of K - k_mean is combined through LDS, then
-//               each wave writes the codes of its 32 rows
-//   all waves   the BF16 V tile is staged row-major in LDS; each 16-byte
-//               output chunk then gathers 16 rows of one channel in the PV
-//               operand order
-// Blocks past the last K/V tile (t >= T, only when Q is quantized: the Q
-// padding reaches 64*Tq >= 64*T rows) write the all-padding Q groups.
 // Absolute maximum of K - k_mean over one lane's 64 channels of a row held as
 // BF16 words (kraw[kk][e]: channels 32kk + 16*(l/32) + 8e + 0..7); kmp points
 // at the lane's first k_mean channel.
@@ -216,6 +204,19 @@ __device__ __forceinline__ float k_row_amax(const uint4 (&kraw)[4][2], const flo
     return am;
 }
 
+// One block of 256 threads per (b, h, 64-row tile t) quantizes everything the
+// tile's rows hold, so each projection row segment is read once:
+//   waves 0, 1  Q groups 2t and 2t+1 (when Q is quantized here): lane l reads
+//               row 32g + l%32, channels 32kk + 16*(l/32) + 0..15, exactly the
+//               16 bytes it writes for kk
+//   waves 2, 3  K rows 64t + 32*(w-2) + l%32, same channel split; the tile's
+//               absolute maximum of K - k_mean is combined through LDS, then
+//               each wave writes the codes of its 32 rows
+//   all waves   the BF16 V tile is staged row-major in LDS; each 16-byte
+//               output chunk then gathers 16 rows of one channel in the PV
+//               operand order
+// Blocks past the last K/V tile (t >= T, only when Q is quantized: the Q
+// padding reaches 64*Tq >= 64*T rows) write the all-padding Q groups.
 template <bool kNormRope>
 __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
     __shared__ uint16_t tile[kBK * kVRow];
