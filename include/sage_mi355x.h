@@ -26,12 +26,18 @@
  *     no state except a thread-local error message.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.  A kernel fault surfaces at
- *     the caller's next synchronisation of that stream.
+ *     the caller's next synchronisation of that stream.  Nothing but kernels
+ *     on `stream` is issued (no copies, fills or host waits), so the calls
+ *     can be captured in a HIP graph.
  *   - Arguments are validated on the host before anything is launched; on
  *     error nothing is launched and a status other than SAGE_OK is returned,
  *     with detail in sage_last_error_message().  No exception crosses the ABI.
  *   - Inputs must be finite BF16 values; non-finite inputs give unspecified
- *     (but memory-safe) results.
+ *     (but memory-safe) results.  Outputs follow the step-by-step definition
+ *     to within the E4M3 rounding of the probabilities while the largest
+ *     score of every row, in log2 units (score * sm_scale * log2(e)), stays
+ *     below about 2^17; beyond that they remain finite but drift from it by
+ *     more (the score step keeps log2(448) - max in one FP32 number).
  */
 #ifndef SAGE_MI355X_H
 #define SAGE_MI355X_H
