@@ -11,6 +11,9 @@
  *       IN: Q, K, V as BF16 bits, each contiguous [B][N][H][128]; the
  *       one-call sage_attn_fwd with sm_scale = 1/sqrt(128) on the default
  *       stream; OUT: O as BF16 bits [B][N][H][128]
+ *   sage_c_consumer run2 IN OUT B N H
+ *       the same through the two calls: sage_quantized_carve,
+ *       sage_quantize_qkv, then sage_attn_fwd_quantized
  * Prints "ok" and exits 0 on success.
  */
 #include <stdint.h>
@@ -71,7 +74,7 @@ static int errors_only(void)
     return 0;
 }
 
-static int run(const char* in_path, const char* out_path, int B, int N, int H)
+static int run(const char* in_path, const char* out_path, int B, int N, int H, int two_calls)
 {
     const size_t elems = (size_t)B * N * H * 128, bytes = elems * 2;
     uint16_t* host = (uint16_t*)malloc(3 * bytes);
@@ -95,8 +98,19 @@ static int run(const char* in_path, const char* out_path, int B, int N, int H)
     sage_bf16_in qi = {q, sb, sn, sh}, ki = {k, sb, sn, sh}, vi = {v, sb, sn, sh};
     sage_bf16_out oo = {o, sb, sn, sh};
     const float sm_scale = (float)(1.0 / sqrt(128.0));
-    sage_status st = sage_attn_fwd(&qi, &ki, &vi, s, sm_scale, &oo, ws, need, NULL);
-    if (st != SAGE_OK) FAIL("sage_attn_fwd: %s: %s", sage_status_string(st), sage_last_error_message());
+    if (two_calls) {
+        sage_quantized qz;
+        sage_status st = sage_quantized_carve(s, ws, need, &qz);
+        if (st != SAGE_OK) FAIL("sage_quantized_carve: %s: %s", sage_status_string(st), sage_last_error_message());
+        st = sage_quantize_qkv(&qi, &ki, &vi, &qz, NULL);
+        if (st != SAGE_OK) FAIL("sage_quantize_qkv: %s: %s", sage_status_string(st), sage_last_error_message());
+        st = sage_attn_fwd_quantized(&qz, sm_scale, &oo, NULL);
+        if (st != SAGE_OK)
+            FAIL("sage_attn_fwd_quantized: %s: %s", sage_status_string(st), sage_last_error_message());
+    } else {
+        sage_status st = sage_attn_fwd(&qi, &ki, &vi, s, sm_scale, &oo, ws, need, NULL);
+        if (st != SAGE_OK) FAIL("sage_attn_fwd: %s: %s", sage_status_string(st), sage_last_error_message());
+    }
     HIPCHK(hipDeviceSynchronize());
     HIPCHK(hipMemcpy(host, o, bytes, hipMemcpyDeviceToHost));
     f = fopen(out_path, "wb");
@@ -115,8 +129,8 @@ static int run(const char* in_path, const char* out_path, int B, int N, int H)
 int main(int argc, char** argv)
 {
     if (argc == 2 && strcmp(argv[1], "errors") == 0) return errors_only();
-    if (argc == 7 && strcmp(argv[1], "run") == 0)
-        return run(argv[2], argv[3], atoi(argv[4]), atoi(argv[5]), atoi(argv[6]));
-    fprintf(stderr, "usage: %s errors | run IN OUT B N H\n", argv[0]);
+    if (argc == 7 && (strcmp(argv[1], "run") == 0 || strcmp(argv[1], "run2") == 0))
+        return run(argv[2], argv[3], atoi(argv[4]), atoi(argv[5]), atoi(argv[6]), strcmp(argv[1], "run2") == 0);
+    fprintf(stderr, "usage: %s errors | run IN OUT B N H | run2 IN OUT B N H\n", argv[0]);
     return 2;
 }

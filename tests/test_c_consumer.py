@@ -1,7 +1,7 @@
 """A plain C program (tests/c_consumer/sage_c_consumer.c) drives the library
 through its C ABI alone: host-side validation on the CPU; on the GPU, the
-one-call path on seeded inputs against the oracle (same bar as the Python
-binding's parity tests)."""
+one-call path and the two-call path on seeded inputs against the oracle
+(same bar as the Python binding's parity tests)."""
 import os
 import subprocess
 import sys
@@ -30,18 +30,21 @@ def test_c_consumer_validation(consumer):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("mode", ["run", "run2"])
 @pytest.mark.parametrize("B,N,H", [(1, 200, 2), (2, 129, 3)])
-def test_c_consumer_one_call_matches_oracle(consumer, tmp_path, B, N, H):
+def test_c_consumer_matches_oracle(consumer, tmp_path, B, N, H, mode):
+    """mode "run": the one-call sage_attn_fwd; "run2": carve, sage_quantize_qkv
+    and sage_attn_fwd_quantized."""
     import torch
     import oracle
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    print("c consumer: B=%d N=%d H=%d" % (B, N, H), flush=True)
+    print("c consumer %s: B=%d N=%d H=%d" % (mode, B, N, H), flush=True)
     inp = workloads.generate(workloads.Workload("c", B, N, H, seed=300 + N))
     bits = [t.contiguous().view(torch.int16).numpy().view(np.uint16) for t in (inp.q, inp.k, inp.v)]
     src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
     np.concatenate([b.ravel() for b in bits]).tofile(src)
-    res = subprocess.run([consumer, "run", str(src), str(dst), str(B), str(N), str(H)],
+    res = subprocess.run([consumer, mode, str(src), str(dst), str(B), str(N), str(H)],
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stderr
     got = oracle.bf16_decode(np.fromfile(dst, np.uint16).reshape(B, N, H, 128)).astype(np.float64)
