@@ -143,3 +143,36 @@ def test_one_call_norm_rope_equals_two_call(sage, name):
     two = sage.attn_fwd_quantized(sage.quantize_qkv_norm_rope(q, k, v, *nrp, p.eps))
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+
+def test_norm_rope_offsets_beyond_2gib(sage):
+    """B = 1, H = 4100, N = 4096 (each input 2.15e9 elements, INT8 Q and K
+    regions 2.15 GB): with the producer on, every quantized byte, scale and
+    the K mean of heads 0 and 4095..4099 bit-identical to the oracle's steps
+    0-4 run on just those heads (heads are independent; the angle tables are
+    per token)."""
+    import oracle
+    B, N, H = 1, 4096, 4100
+    gen = torch.Generator(device="cuda").manual_seed(79)
+    q = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((B, N, H, 128), generator=gen, device="cuda", dtype=torch.bfloat16)
+    p = workloads.norm_rope_params(N, seed=81)
+    nrp = [t.cuda() for t in (p.q_weight, p.k_weight, p.cos, p.sin)]
+    qz = sage.quantize_qkv_norm_rope(q, k, v, *nrp, p.eps)
+    torch.cuda.synchronize()
+    G, T = qz.G, qz.T
+    assert (H - 1) * G * 4096 >= 2 ** 31 and (H - 1) * N * 128 >= 2 ** 31
+    for h in [0, 4095, 4096, 4097, 4098, 4099]:
+        qh, kh, vh = (t[:, :, h:h + 1].cpu() for t in (q, k, v))
+        ref = oracle.quantize_norm_rope(qh, kh, vh, p.q_weight, p.k_weight, p.cos, p.sin, p.eps)
+        assert np.array_equal(_bits(qz.k_mean[0, h].cpu().numpy()), _bits(ref.k_mean.reshape(-1)))
+        assert np.array_equal(_bits(qz.q_scale[0, h].cpu().numpy()), _bits(ref.q_scale.reshape(-1)))
+        assert np.array_equal(_bits(qz.k_scale[0, h].cpu().numpy()), _bits(ref.k_scale.reshape(-1)))
+        assert np.array_equal(_bits(qz.v_scale[0, h].cpu().numpy()), _bits(ref.v_scale.reshape(-1)))
+        gq = layouts.q_logical(qz.q_i8[h * G * 4096:(h + 1) * G * 4096].cpu().numpy(), 1, 1, N)
+        gk = layouts.k_logical(qz.k_i8[h * T * 8192:(h + 1) * T * 8192].cpu().numpy(), 1, 1, N)
+        gv = layouts.v_logical(qz.v_fp8[h * T * 8192:(h + 1) * T * 8192].cpu().numpy(), 1, 1, N)
+        assert np.array_equal(gq, ref.q_i8) and np.array_equal(gk, ref.k_i8) and np.array_equal(gv, ref.v8)
+    _log("norm+rope offsets beyond 2 GiB: heads 0, 4095..4099 bit-exact")
