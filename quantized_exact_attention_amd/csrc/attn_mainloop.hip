@@ -280,6 +280,20 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     const bool active = g < a.g_end && g * kQG < a.N;
     const int T = a.T;
 
+    const int8_t* kg = a.k_i8 + (int64_t)bh * T * kTileBytes;
+    const int8_t* vg = (const int8_t*)a.v_fp8 + (int64_t)bh * T * kTileBytes;
+    const const_f32_ptr ksc = (const_f32_ptr)(a.k_scale + (int64_t)bh * T);
+    const float c = a.c;
+
+    // Prologue: K(0..2) and V(0..1) to LDS (issued first, so that they are in
+    // flight while the wave loads, or quantizes, its Q group), then QK of
+    // tile 0.  Loads past the last tile are clamped to it and land in slots
+    // that are never read again.
+    tile_to_lds(kg, lds_k, voff, wave);
+    tile_to_lds(vg, lds_v, voff, wave);
+    tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, voff, wave);
+    tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, voff, wave);
+    tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, voff, wave);
     v4i qf[4];
     float qs = 0.0f;
     if (a.q_bf16) {
@@ -318,19 +332,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
         for (int kk = 0; kk < 4; ++kk) qf[kk] = v4i{0, 0, 0, 0};
     }
 
-    const int8_t* kg = a.k_i8 + (int64_t)bh * T * kTileBytes;
-    const int8_t* vg = (const int8_t*)a.v_fp8 + (int64_t)bh * T * kTileBytes;
-    const const_f32_ptr ksc = (const_f32_ptr)(a.k_scale + (int64_t)bh * T);
-    const float c = a.c;
-
-    // Prologue: K(0..2) and V(0..1) to LDS, then QK of tile 0.  Loads past
-    // the last tile are clamped to it and land in slots that are never read
-    // again.
-    tile_to_lds(kg, lds_k, voff, wave);
-    tile_to_lds(vg, lds_v, voff, wave);
-    tile_to_lds(kg + (int64_t)min(1, T - 1) * kTileBytes, lds_k + kTileBytes, voff, wave);
-    tile_to_lds(kg + (int64_t)min(2, T - 1) * kTileBytes, lds_k + 2 * kTileBytes, voff, wave);
-    tile_to_lds(vg + (int64_t)min(1, T - 1) * kTileBytes, lds_v + kTileBytes, voff, wave);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     v16i s0, s1;
