@@ -34,10 +34,16 @@
  *     with detail in sage_last_error_message().  No exception crosses the ABI.
  *   - Inputs must be finite BF16 values; non-finite inputs give unspecified
  *     (but memory-safe) results.  Outputs follow the step-by-step definition
- *     to within the E4M3 rounding of the probabilities while the largest
- *     score of every row, in log2 units (score * sm_scale * log2(e)), stays
- *     below about 2^17; beyond that they remain finite but drift from it by
- *     more (the score step keeps log2(448) - max in one FP32 number).
+ *     below up to the hardware exp2 and the order of FP32 sums, which can move
+ *     a probability to the adjacent E4M3 code at a rounding midpoint.  A
+ *     32-row query group whose scores are bounded by 2^12 in log2 units
+ *     (score * sm_scale * log2(e); the bound is 127 * the largest L1 norm of
+ *     the group's Q codes * q_scale * the head's largest k_scale * sm_scale *
+ *     log2(e)) forms each probability as 2^(S*sj + log2(448) - m) with a single
+ *     rounding; every other group takes the definition's three roundings one
+ *     by one, for any finite input.  Where an intermediate of the definition
+ *     overflows FP32 (input magnitudes near the BF16 range), the outputs do
+ *     too.
  */
 #ifndef SAGE_MI355X_H
 #define SAGE_MI355X_H

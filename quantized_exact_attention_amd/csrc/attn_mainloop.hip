@@ -47,6 +47,9 @@ constexpr int kTileLoads = kTileBytes / (kWaves * 1024);
 static_assert(kTileLoads * kWaves * 1024 == kTileBytes, "tile split");
 constexpr float kLog2Of448 = 8.8073549220576041f;  // log2(448)
 
+// Scheduling fence: the compiler moves no instruction across it.
+#define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // Bijection from dispatch order to work items such that the items dispatched
 // to one XCD (dispatch index mod 8) are consecutive.
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
@@ -68,11 +71,12 @@ __device__ __forceinline__ float unbias(int s) { return __int_as_float(s) - kSco
 
 // QK of one wave against one staged K tile: s0 = S^T for keys 0..31, s1 for
 // keys 32..63 (register r of lane l: key 8*(r/4) + 4*(l/32) + r%4 of its
-// block, query row l%32 of the wave's group), exact int32 plus `init`.
-__device__ __forceinline__ void qk_tile(const int8_t* ktile, const v4i (&qf)[4], int lane,
-                                        v16i& s0, v16i& s1, int init) {
-    s0 = v16i{init, init, init, init, init, init, init, init, init, init, init, init, init, init, init, init};
-    s1 = s0;
+// block, query row l%32 of the wave's group), exact int32 plus the initial
+// accumulator `init` (the mainloop passes the score bias below).
+__device__ __forceinline__ void qk_tile(const int8_t* ktile, const v4i (&qf)[4], int lane, v16i& s0, v16i& s1,
+                                        const v16i& init) {
+    s0 = init;
+    s1 = init;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const v4i a0 = *(const v4i*)(ktile + ((0 * 4 + kk) * 64 + lane) * 16);
@@ -114,22 +118,21 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
 // gives the largest score), alpha = 2^(m - m_new), p = 448 * 2^(t - m_new),
 // this lane's part of the denominator, and the FP8 codes packed in the
 // B-operand order of the PV instruction.  kLast masks keys at or beyond
-// `tail` in the final, partial tile.
+// `tail` in the final, partial tile.  `moved` reports that some row maximum
+// of the wave moved, which is also exactly when RO needs the alpha rescale.
 //
-// p = 2^fma(S, sj, off) with 448 folded into off = log2(448) - m.  off is
-// kept across tiles and recomputed only when some row maximum of the wave
-// moves; `moved` reports that, which is also exactly when RO needs the alpha
-// rescale.  For the largest score the exponent is log2(448) plus the rounding
-// errors of m and of off, about one unit in the last place of m together.
-// That is negligible for the maxima of real attention (|m| below 2^5 in log2
-// units in the pages' workloads); from |m| = 2^17 on it reaches 2^-6 and the
-// outputs move visibly away from those of the stepwise rounding; from
-// |m| = 2^20 on it can lift the largest p past 464, which converts to NaN.
-// There off is lowered by two units in the last place of m, which keeps every
-// p at or below 448.
-constexpr float kOffsetGuardFrom = 1048576.0f;   // 2^20
-
-template <bool kLast>
+// Two forms of the score step (kStepwise), one per wave for the whole loop:
+//   * stepwise, the definition's roundings one by one: t = fl(S * sj),
+//     x = fl(t - m), p = fl(448 * 2^x);
+//   * fused, two vector instructions fewer per score: p = 2^fma(S, sj, off)
+//     with off = log2(448) - m, kept across tiles and recomputed when a row
+//     maximum moves.  It rounds once where the stepwise form rounds three
+//     times; the two differ by about one unit in the last place of m,
+//     relative, in p.  The fused form is taken only by waves whose scores are
+//     all bounded by 2^12 in magnitude (in log2 units, see
+//     kStepwiseFrom), where that difference is below 2^-11 of p, a small
+//     fraction of an E4M3 step; real attention has |m| of a few units.
+template <bool kStepwise, bool kLast>
 __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int tail, int lane, float& m,
                                              float& off, float& dpart, float& alpha, bool& moved, v8i& pk) {
     if (kLast) {
@@ -153,19 +156,20 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
     if (moved) {
         alpha = __builtin_amdgcn_exp2f(m - m_new);
         dpart *= alpha;
-        off = kLog2Of448 - m_new;
-        if (!(__builtin_fabsf(m_new) < kOffsetGuardFrom)) {
-            // two units in the last place of m (|m| >= 2^20 is a normal number)
-            const float u2 = __int_as_float((__float_as_int(m_new) & 0x7F800000) - (22 << 23));
-            off -= u2;
-        }
+        if (!kStepwise) off = kLog2Of448 - m_new;
     }
     m = m_new;
     float p[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s0[r]), sj, off));
-        p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s1[r]), sj, off));
+        if (kStepwise) {
+            const float t0 = unbias(s0[r]) * sj, t1 = unbias(s1[r]) * sj;
+            p[r] = 448.0f * __builtin_amdgcn_exp2f(t0 - m);
+            p[16 + r] = 448.0f * __builtin_amdgcn_exp2f(t1 - m);
+        } else {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s0[r]), sj, off));
+            p[16 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(unbias(s1[r]), sj, off));
+        }
     }
     if (kLast) {
 #pragma unroll
@@ -190,6 +194,11 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
         pk[v] = cvt_pk_e4m3<true>(p[4 * v + 2], p[4 * v + 3], w);
     }
 }
+
+// Scores of magnitude at or above this (log2 units) take the stepwise form.
+// A wave takes the fused form only when a bound on all of its scores lies
+// below it (see the kernel's prologue).
+constexpr float kStepwiseFrom = 4096.0f;   // 2^12
 
 __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
 #pragma unroll
@@ -260,7 +269,111 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // counter that tracks the tile loads in flight.
 typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
-#define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
+// What the prologue hands to the tile loop of one wave.
+struct WaveCtx {
+    const int8_t* kg;      // the head's K tiles
+    const int8_t* vg;      // the head's V tiles
+    const_f32_ptr ksc;     // the head's K scales (scalar loads)
+    int8_t* lds_k;
+    int8_t* lds_v;
+    uint32_t voff;         // this lane's byte offset for the tile loads
+    int wave, lane;
+    bool active;           // the wave's 32-row group holds rows < N of the range
+    float qs;              // the group's Q scale
+    int g, b, hl, bh;      // group, batch entry, head within the range, b*H + h
+};
+
+// One wave from the QK of tile 0 to its stored output rows, in one form of
+// the score step: the tile loop, the last (partial) tile, then 1/d, the V
+// scale and BF16 into token-major rows.  Inactive waves (query groups beyond
+// the rows) issue their share of every tile load and take every barrier, and
+// compute nothing.
+//
+// Ring slots by role, rotated each iteration: kq holds K(j+1) for this
+// iteration's QK, kn K(j+2), and kf receives K(j+3); vc holds V(j) for this
+// iteration's PV, vn V(j+1), and vf receives V(j+2).
+template <bool kStepwise>
+__device__ __forceinline__ void attend(const MainloopArgs& a, const WaveCtx& w, const v4i (&qf)[4],
+                                       const v16i& bias) {
+    const int T = a.T;
+    const float c = a.c;
+    const int lane = w.lane;
+    v16i s0, s1;
+    if (w.active) qk_tile(w.lds_k, qf, lane, s0, s1, bias);
+    __syncthreads();   // K slot 0 is refilled in iteration 0
+
+    float m = -INFINITY;
+    float off = 0.0f;      // fused form: log2(448) - m, set when m first moves
+    float dpart = 0.0f;    // this lane's share of the row denominator
+    v16f ro[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ro[db][r] = 0.0f;
+    int8_t* kq = w.lds_k + kTileBytes;
+    int8_t* kn = w.lds_k + 2 * kTileBytes;
+    int8_t* kf = w.lds_k;
+    int8_t* vc = w.lds_v;
+    int8_t* vn = w.lds_v + kTileBytes;
+    int8_t* vf = w.lds_v + 2 * kTileBytes;
+    for (int j = 0; j < T - 1; ++j) {
+        tile_to_lds(w.kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, w.voff, w.wave);
+        tile_to_lds(w.vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, w.voff, w.wave);
+        if (w.active) {
+            // softmax of tile j, the alpha rescale of RO (skipped when no row
+            // of the wave changed its max), PV of tile j, QK of tile j+1
+            float alpha;
+            v8i pk;
+            bool moved;
+            softmax_tile<kStepwise, false>(s0, s1, (w.qs * w.ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
+            if (moved) rescale(ro, alpha);
+            SAGE_FENCE();
+            pv_tile(vc, pk, lane, ro);
+            qk_tile(kq, qf, lane, s0, s1, bias);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
+        block_barrier();
+        int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
+        t = vf;  vf = vc;  vc = vn;  vn = t;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (!w.active) return;
+    {
+        const int j = T - 1;
+        float alpha;
+        v8i pk;
+        bool moved;
+        softmax_tile<kStepwise, true>(s0, s1, (w.qs * w.ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha,
+                                      moved, pk);
+        if (moved) rescale(ro, alpha);
+        pv_tile(vc, pk, lane, ro);                   // V(T-1)
+    }
+
+    const float dtot = halves_sum(dpart);
+    const float rcp = 1.0f / dtot;
+    const int n = w.g * kQG + (lane & 31);
+    if (n < a.q_start || n >= a.q_end) return;
+    uint16_t* op = a.o + w.b * a.o_sb + (int64_t)(n - a.q_start) * a.o_sn + w.hl * a.o_sh;
+    const float* vs = a.v_scale + (int64_t)w.bh * kHD;
+    const int h4 = 4 * (lane >> 5);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int d0 = 32 * db + 8 * rr + h4;
+            const v4f s4 = *(const v4f*)(vs + d0);
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (ro[db][4 * rr + i] * rcp) * s4[i];
+            const v2bf lo = v2bf{(__bf16)o[0], (__bf16)o[1]};
+            const v2bf hi = v2bf{(__bf16)o[2], (__bf16)o[3]};
+            uint2 wv;
+            wv.x = __builtin_bit_cast(uint32_t, lo);
+            wv.y = __builtin_bit_cast(uint32_t, hi);
+            *(uint2*)(op + d0) = wv;
+        }
+    }
+}
 
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(MainloopArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
@@ -332,20 +445,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
         for (int kk = 0; kk < 4; ++kk) qf[kk] = v4i{0, 0, 0, 0};
     }
 
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    v16i s0, s1;
-    if (active) qk_tile(lds_k, qf, lane, s0, s1, kScoreBias);
-    __syncthreads();   // K slot 0 is refilled in iteration 0
-
-    float m = -INFINITY;
-    float off = 0.0f;      // log2(448) - m, set when m first moves
-    float dpart = 0.0f;    // this lane's share of the row denominator
-    v16f ro[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ro[db][r] = 0.0f;
     // the initial QK accumulator, kept in registers for the whole loop (the
     // empty asm hides the constant from the compiler, which would otherwise
     // rebuild it every iteration)
@@ -353,84 +452,44 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
                      kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
                      kScoreBias, kScoreBias};
     asm volatile("" : "+v"(bias));
-    // Ring slots by role, rotated each iteration: kq holds K(j+1) for this
-    // iteration's QK, kn K(j+2), and kf receives K(j+3); vc holds V(j) for
-    // this iteration's PV, vn V(j+1), and vf receives V(j+2).
-    int8_t* kq = lds_k + kTileBytes;
-    int8_t* kn = lds_k + 2 * kTileBytes;
-    int8_t* kf = lds_k;
-    int8_t* vc = lds_v;
-    int8_t* vn = lds_v + kTileBytes;
-    int8_t* vf = lds_v + 2 * kTileBytes;
-    for (int j = 0; j < T - 1; ++j) {
-        tile_to_lds(kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, voff, wave);
-        tile_to_lds(vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, voff, wave);
-        if (active) {
-            // softmax of tile j, the alpha rescale of RO (skipped when no row
-            // of the wave changed its max), PV of tile j, QK of tile j+1
-            float alpha;
-            v8i pk;
-            bool moved;
-            softmax_tile<false>(s0, s1, (qs * ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
-            if (moved) rescale(ro, alpha);
-            SAGE_FENCE();
-            pv_tile(vc, pk, lane, ro);
-            s0 = bias;
-            s1 = bias;
+
+    // The score step's form for this wave (wave-uniform).  Every code has
+    // |code| <= 127, so |S| <= 127 * ||q||_1 for each query row q of the
+    // group and every key, and |t| = |S| * sj <= 127 * max ||q||_1 * qs *
+    // max_t k_scale[t] * c over every tile of the head.  The fused form is
+    // taken when that bound is below kStepwiseFrom.  ||q||_1 comes from the
+    // codes in registers (v_sad_u8 on the codes shifted to offset binary);
+    // the K scale maximum from one pass over the head's T scales.
+    uint32_t l1 = 0;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const v4i a0 = *(const v4i*)(kq + ((0 * 4 + kk) * 64 + lane) * 16);
-                const v4i a1 = *(const v4i*)(kq + ((1 * 4 + kk) * 64 + lane) * 16);
-                s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qf[kk], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qf[kk], s1, 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
-        block_barrier();
-        int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
-        t = vf;  vf = vc;  vc = vn;  vn = t;
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l1 = __builtin_amdgcn_sad_u8((uint32_t)qf[kk][e] ^ 0x80808080u, 0x80808080u, l1);
+    l1 += (uint32_t)__shfl_xor((int)l1, 32, 64);            // the row's other 64 channels
+    uint32_t ksmax = 0;                                       // scales are >= 0: compare their bits
+    for (int t = lane; t < T; t += 64) ksmax = max(ksmax, __float_as_uint(a.k_scale[(int64_t)bh * T + t]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        l1 = max(l1, (uint32_t)__shfl_xor((int)l1, o, 64));
+        ksmax = max(ksmax, (uint32_t)__shfl_xor((int)ksmax, o, 64));
     }
+    const float bound = ((127.0f * (float)l1) * qs) * (__uint_as_float(ksmax) * c);
+    const bool stepwise = __builtin_amdgcn_readfirstlane(!(bound < kStepwiseFrom)) != 0;
+
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-    if (!active) return;
-    {
-        const int j = T - 1;
-        float alpha;
-        v8i pk;
-        bool moved;
-        softmax_tile<true>(s0, s1, (qs * ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha, moved, pk);
-        if (moved) rescale(ro, alpha);
-        pv_tile(vc, pk, lane, ro);                   // V(T-1)
-    }
-
-    const float dtot = halves_sum(dpart);
-    const float rcp = 1.0f / dtot;
-    const int n = g * kQG + (lane & 31);
-    if (n < a.q_start || n >= a.q_end) return;
-    uint16_t* op = a.o + b * a.o_sb + (int64_t)(n - a.q_start) * a.o_sn + hl * a.o_sh;
-    const float* vs = a.v_scale + (int64_t)bh * kHD;
-    const int h4 = 4 * (lane >> 5);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int d0 = 32 * db + 8 * rr + h4;
-            const v4f s4 = *(const v4f*)(vs + d0);
-            float o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (ro[db][4 * rr + i] * rcp) * s4[i];
-            const v2bf lo = v2bf{(__bf16)o[0], (__bf16)o[1]};
-            const v2bf hi = v2bf{(__bf16)o[2], (__bf16)o[3]};
-            uint2 wv;
-            wv.x = __builtin_bit_cast(uint32_t, lo);
-            wv.y = __builtin_bit_cast(uint32_t, hi);
-            *(uint2*)(op + d0) = wv;
-        }
-    }
+    __syncthreads();
+    // Each form runs from here to the stored output in its own copy of the
+    // code, which keeps the register allocation of the two loops apart.
+    const WaveCtx w{kg, vg, ksc, lds_k, lds_v, voff, wave, lane, active, qs, g, b, hl, bh};
+    if (stepwise)
+        attend<true>(a, w, qf, bias);
+    else
+        attend<false>(a, w, qf, bias);
 }
 
-// One wave per (b, h, group g, tile t): the same QK tile routine as the
-// mainloop, written out as int32 for inspection.
+// One wave per (b, h, group g, tile t): the mainloop's QK tile routine with
+// the mainloop's initial accumulator, written out as int32 (bias removed)
+// for inspection.
 __global__ __launch_bounds__(64) void debug_qk_kernel(DebugQkArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t kt[kTileBytes];
     const int g = blockIdx.x, t = blockIdx.y, bh = blockIdx.z;
@@ -444,14 +503,17 @@ __global__ __launch_bounds__(64) void debug_qk_kernel(DebugQkArgs a) {
     const int8_t* qp = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const v4i*)(qp + kk * 1024);
+    const v16i bias = v16i{kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
+                           kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias, kScoreBias,
+                           kScoreBias, kScoreBias};
     v16i s0, s1;
-    qk_tile(kt, qf, lane, s0, s1, 0);
+    qk_tile(kt, qf, lane, s0, s1, bias);
     const int64_t Nq = (int64_t)a.G * kQG, Nk = (int64_t)a.T * kBK;
     int32_t* out = a.s_out + ((int64_t)bh * Nq + g * kQG + (lane & 31)) * Nk + (int64_t)t * kBK;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        out[key_of(0, r, lane)] = s0[r];
-        out[key_of(1, r, lane)] = s1[r];
+        out[key_of(0, r, lane)] = s0[r] - kScoreBias;
+        out[key_of(1, r, lane)] = s1[r] - kScoreBias;
     }
 }
 

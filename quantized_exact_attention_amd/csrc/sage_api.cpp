@@ -1,6 +1,6 @@
 // sage_api.cpp -- the C ABI declared in include/sage_mi355x.h: host-side
 // validation, workspace carving and kernel launches on the caller's stream.
-#include "../../include/sage_mi355x.h"
+#include "sage_mi355x.h"
 
 #include <hip/hip_runtime.h>
 
