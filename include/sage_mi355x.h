@@ -55,8 +55,9 @@
 extern "C" {
 #endif
 
-/* 2: adds sage_quantize_qkv_norm_rope and sage_attn_fwd_norm_rope (additions only). */
-#define SAGE_ABI_VERSION 2
+/* 2: adds sage_quantize_qkv_norm_rope and sage_attn_fwd_norm_rope (additions only).
+ * 3: sage_quantized gains k_scale_max (the struct grows; rebuild callers). */
+#define SAGE_ABI_VERSION 3
 #define SAGE_HEAD_DIM 128
 
 typedef enum sage_status {
@@ -115,6 +116,9 @@ typedef struct sage_bf16_out {
  *   k_tile_sum, v_tile_amax  FP32 [B][H][T][128], v_inv FP32 [B][H][128]:
  *           scratch of the prepass (per-tile K channel sums, per-tile V
  *           channel absolute maxima, per-channel 448/amax).
+ *   k_scale_max FP32 [B][H]: the largest k_scale of each (b, h), written by
+ *           the prepass; the mainloop reads it to bound its scores (see the
+ *           conventions above).
  *
  * The INT8 and E4M3 layouts are the operand layouts of the gfx950 matrix
  * instructions the mainloop issues, so every mainloop load is a contiguous
@@ -131,6 +135,7 @@ typedef struct sage_quantized {
     float* k_tile_sum;
     float* v_tile_amax;
     float* v_inv;
+    float* k_scale_max;
 } sage_quantized;
 
 /* Bytes of workspace sage_quantized_carve() and sage_attn_fwd() need for

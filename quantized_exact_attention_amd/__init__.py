@@ -16,10 +16,12 @@ from . import build as _build
 
 __all__ = [
     "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv", "quantize_qkv_norm_rope",
-    "attn_fwd_quantized", "attn_fwd", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3", "default_sm_scale",
+    "attn_fwd_quantized", "attn_fwd", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3",
+    "default_sm_scale",
 ]
 
 HEAD_DIM = 128
+ABI_VERSION = 3   # SAGE_ABI_VERSION of include/sage_mi355x.h that these structures follow
 
 
 class SageError(RuntimeError):
@@ -50,7 +52,8 @@ class _Quantized(ctypes.Structure):
                 ("q_i8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
                 ("k_i8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p),
                 ("v_fp8", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("k_tile_sum", ctypes.c_void_p), ("v_tile_amax", ctypes.c_void_p), ("v_inv", ctypes.c_void_p)]
+                ("k_tile_sum", ctypes.c_void_p), ("v_tile_amax", ctypes.c_void_p), ("v_inv", ctypes.c_void_p),
+                ("k_scale_max", ctypes.c_void_p)]
 
 
 class _NormRope(ctypes.Structure):
@@ -105,6 +108,9 @@ def _load():
     lib.sage_debug_qk_s32.restype = st
     lib.sage_debug_cvt_e4m3.argtypes = [P, P, ctypes.c_int64, P]
     lib.sage_debug_cvt_e4m3.restype = st
+    if lib.sage_abi_version() != ABI_VERSION:
+        raise SageError("%s has ABI version %d, this binding needs %d (rebuild the library)"
+                        % (_build.LIB, lib.sage_abi_version(), ABI_VERSION))
     _lib = lib
     return lib
 
@@ -208,6 +214,10 @@ class Quantized:
     @property
     def k_scale(self):
         return self._view("k_scale", _torch().float32, self.B * self.H * self.T).view(self.B, self.H, self.T)
+
+    @property
+    def k_scale_max(self):
+        return self._view("k_scale_max", _torch().float32, self.B * self.H).view(self.B, self.H)
 
     @property
     def k_mean(self):

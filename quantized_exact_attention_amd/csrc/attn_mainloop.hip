@@ -149,11 +149,19 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
         ma = max(max(ma, s0[r]), s0[r + 1]);
         mb = max(max(mb, s1[r]), s1[r + 1]);
     }
-    const int mx = halves_max(max(ma, mb)) - kScoreBias;
-    const float m_new = fmaxf(m, (float)mx * sj);
-    moved = __any(m_new != m);
+    // the tile's largest score of the row, t = fl(S * sj) of the largest S
+    // (unbias is exact); a compare and a select rather than fmaxf, which
+    // would add a NaN-quieting instruction (m and t are never NaN here)
+    const float tmax = unbias(halves_max(max(ma, mb))) * sj;
+    const bool up = tmax > m;
+    const float m_new = up ? tmax : m;
+    moved = __any(up);
     alpha = 1.0f;           // 2^(m - m_new) is exactly 1 where m does not move
     if (moved) {
+        // A real branch: the empty volatile asm keeps the compiler from
+        // turning this block into selects, which would run its exp2 on every
+        // tile (about 80% of tiles move no maximum).
+        asm volatile("");
         alpha = __builtin_amdgcn_exp2f(m - m_new);
         dpart *= alpha;
         if (!kStepwise) off = kLog2Of448 - m_new;
@@ -178,6 +186,8 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
             if (key_of(1, r, lane) >= tail) p[16 + r] = 0.0f;
         }
     }
+    // this lane's share of the denominator (four chains over the 32 values,
+    // three of them started from a value rather than from zero)
     float d0 = dpart, d1 = p[1], d2 = p[2], d3 = p[3];
     d0 += p[0];
 #pragma unroll
@@ -458,22 +468,18 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     // group and every key, and |t| = |S| * sj <= 127 * max ||q||_1 * qs *
     // max_t k_scale[t] * c over every tile of the head.  The fused form is
     // taken when that bound is below kStepwiseFrom.  ||q||_1 comes from the
-    // codes in registers (v_sad_u8 on the codes shifted to offset binary);
-    // the K scale maximum from one pass over the head's T scales.
+    // codes in registers (v_sad_u8 on the codes shifted to offset binary),
+    // the head's largest K scale from the prepass.
     uint32_t l1 = 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) l1 = __builtin_amdgcn_sad_u8((uint32_t)qf[kk][e] ^ 0x80808080u, 0x80808080u, l1);
     l1 += (uint32_t)__shfl_xor((int)l1, 32, 64);            // the row's other 64 channels
-    uint32_t ksmax = 0;                                       // scales are >= 0: compare their bits
-    for (int t = lane; t < T; t += 64) ksmax = max(ksmax, __float_as_uint(a.k_scale[(int64_t)bh * T + t]));
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        l1 = max(l1, (uint32_t)__shfl_xor((int)l1, o, 64));
-        ksmax = max(ksmax, (uint32_t)__shfl_xor((int)ksmax, o, 64));
-    }
-    const float bound = ((127.0f * (float)l1) * qs) * (__uint_as_float(ksmax) * c);
+    for (int o = 16; o >= 1; o >>= 1) l1 = max(l1, (uint32_t)__shfl_xor((int)l1, o, 64));
+    const float ksmax = ((const_f32_ptr)a.k_scale_max)[bh];
+    const float bound = ((127.0f * (float)l1) * qs) * (ksmax * c);
     const bool stepwise = __builtin_amdgcn_readfirstlane(!(bound < kStepwiseFrom)) != 0;
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);

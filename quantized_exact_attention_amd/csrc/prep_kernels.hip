@@ -180,6 +180,7 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     }
     a.v_scale[(int64_t)bh * kHD + d] = scale;
     a.v_inv[(int64_t)bh * kHD + d] = inv;
+    if (d == 0) a.k_scale_max[bh] = 0.0f;    // the quantizer raises it tile by tile
 }
 
 // Absolute maximum of K - k_mean over one lane's 64 channels of a row held as
@@ -345,7 +346,12 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
             if (kn >= a.N) codes = make_uint4(0, 0, 0, 0);
             *(uint4*)(out + (half * 4 + kk) * 64 * 16) = codes;
         }
-        if (wave == 2 && lane == 0) a.k_scale[(int64_t)bh * a.T + t] = scale;
+        if (wave == 2 && lane == 0) {
+            a.k_scale[(int64_t)bh * a.T + t] = scale;
+            // the head's largest K scale: scales are >= 0, so their bit
+            // patterns order as the values do
+            atomicMax((unsigned int*)a.k_scale_max + bh, __float_as_uint(scale));
+        }
     }
 
     uint8_t* out = a.v_fp8 + ((int64_t)bh * a.T + t) * kTileBytes;
@@ -398,7 +404,7 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         FinalizeArgs a;
         a.k_tile_sum = p.k_tile_sum; a.v_tile_amax = p.v_tile_amax;
         a.T = p.T; a.N = p.N;
-        a.k_mean = p.k_mean; a.v_scale = p.v_scale; a.v_inv = p.v_inv;
+        a.k_mean = p.k_mean; a.v_scale = p.v_scale; a.v_inv = p.v_inv; a.k_scale_max = p.k_scale_max;
         hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)BH), dim3(128), 0, stream, a);
     }
     {
@@ -410,6 +416,7 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         a.Tq = p.with_q ? p.G / 2 : p.T;
         a.k_mean = p.k_mean; a.v_inv = p.v_inv; a.v_scale = p.v_scale;
         a.q_i8 = p.q_i8; a.q_scale = p.q_scale; a.k_i8 = p.k_i8; a.k_scale = p.k_scale; a.v_fp8 = p.v_fp8;
+        a.k_scale_max = p.k_scale_max;
         a.nr = p.nr;
         if (p.norm_rope)
             hipLaunchKernelGGL(quant_qkv_kernel<true>, dim3((unsigned)(BH * a.Tq)), dim3(256), 0, stream, a);

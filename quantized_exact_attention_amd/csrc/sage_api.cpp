@@ -51,7 +51,9 @@ bool dims_of(const sage_shape& s, Dims* d) {
 }
 
 // Region sizes in carve order.
-void region_sizes(const Dims& d, size_t out[10]) {
+constexpr int kRegions = 11;
+
+void region_sizes(const Dims& d, size_t out[kRegions]) {
     const size_t BH = (size_t)(d.B * d.H);
     out[0] = BH * d.Nq * 128;              // q_i8
     out[1] = BH * d.G * sizeof(float);     // q_scale
@@ -63,10 +65,11 @@ void region_sizes(const Dims& d, size_t out[10]) {
     out[7] = BH * d.T * 128 * sizeof(float);  // k_tile_sum
     out[8] = BH * d.T * 128 * sizeof(float);  // v_tile_amax
     out[9] = BH * 128 * sizeof(float);     // v_inv
+    out[10] = BH * sizeof(float);          // k_scale_max
 }
 
 size_t total_bytes(const Dims& d) {
-    size_t sz[10];
+    size_t sz[kRegions];
     region_sizes(d, sz);
     size_t t = 0;
     for (size_t x : sz) t += align_up(x);
@@ -102,13 +105,13 @@ sage_status check_quantized(const sage_quantized* qz, Dims* d) {
         return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*2*ceil(N/128)<2^31)",
                     qz->shape.B, qz->shape.N, qz->shape.H, qz->shape.D);
     if (!qz->q_i8 || !qz->q_scale || !qz->k_i8 || !qz->k_scale || !qz->k_mean || !qz->v_fp8 || !qz->v_scale ||
-        !qz->k_tile_sum || !qz->v_tile_amax || !qz->v_inv)
+        !qz->k_tile_sum || !qz->v_tile_amax || !qz->v_inv || !qz->k_scale_max)
         return fail(SAGE_ERR_INVALID_ARGUMENT, "a quantized-operand pointer is NULL");
     const void* p16[] = {qz->q_i8, qz->k_i8, qz->v_fp8, qz->k_mean, qz->v_scale, qz->k_tile_sum, qz->v_tile_amax,
                          qz->v_inv};
     for (const void* p : p16)
         if ((uintptr_t)p % 16) return fail(SAGE_ERR_UNSUPPORTED, "quantized operands must be 16-byte aligned");
-    if ((uintptr_t)qz->q_scale % 4 || (uintptr_t)qz->k_scale % 4)
+    if ((uintptr_t)qz->q_scale % 4 || (uintptr_t)qz->k_scale % 4 || (uintptr_t)qz->k_scale_max % 4)
         return fail(SAGE_ERR_UNSUPPORTED, "scales must be 4-byte aligned");
     return SAGE_OK;
 }
@@ -145,7 +148,7 @@ sage_status prepass(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf1
     p.k = (const uint16_t*)k->data; p.k_sb = k->stride_b; p.k_sn = k->stride_n; p.k_sh = k->stride_h;
     p.v = (const uint16_t*)v->data; p.v_sb = v->stride_b; p.v_sn = v->stride_n; p.v_sh = v->stride_h;
     p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
-    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_mean = qz->k_mean;
+    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_mean = qz->k_mean; p.k_scale_max = qz->k_scale_max;
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.k_tile_sum = qz->k_tile_sum; p.v_tile_amax = qz->v_tile_amax; p.v_inv = qz->v_inv;
     p.norm_rope = nr != nullptr;
@@ -173,7 +176,7 @@ sage_status mainloop(const sage_quantized* qz, float sm_scale, const sage_range*
         return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
     sage::MainloopArgs p;
     p.q_i8 = qz->q_i8; p.q_scale = qz->q_scale;
-    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale;
+    p.k_i8 = qz->k_i8; p.k_scale = qz->k_scale; p.k_scale_max = qz->k_scale_max;
     p.v_fp8 = qz->v_fp8; p.v_scale = qz->v_scale;
     p.q_bf16 = q_src ? (const uint16_t*)q_src->data : nullptr;
     p.q_sb = q_src ? q_src->stride_b : 0; p.q_sn = q_src ? q_src->stride_n : 0; p.q_sh = q_src ? q_src->stride_h : 0;
@@ -250,11 +253,11 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
     if ((uintptr_t)ws % kAlign) return fail(SAGE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     const size_t need = total_bytes(d);
     if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
-    size_t sz[10];
+    size_t sz[kRegions];
     region_sizes(d, sz);
     char* p = (char*)ws;
-    void* r[10];
-    for (int i = 0; i < 10; ++i) {
+    void* r[kRegions];
+    for (int i = 0; i < kRegions; ++i) {
         r[i] = p;
         p += align_up(sz[i]);
     }
@@ -269,6 +272,7 @@ sage_status sage_quantized_carve(sage_shape s, void* ws, size_t ws_bytes, sage_q
     out->k_tile_sum = (float*)r[7];
     out->v_tile_amax = (float*)r[8];
     out->v_inv = (float*)r[9];
+    out->k_scale_max = (float*)r[10];
     return SAGE_OK;
 }
 

@@ -32,6 +32,7 @@ struct FinalizeArgs {
     float* k_mean;
     float* v_scale;
     float* v_inv;
+    float* k_scale_max;   // zeroed here, then raised by the quantizer
 };
 
 struct QuantArgs {
@@ -45,6 +46,7 @@ struct QuantArgs {
     const float* v_scale;
     int8_t* q_i8; float* q_scale;
     int8_t* k_i8; float* k_scale;
+    float* k_scale_max;  // per (b, h): maximum of k_scale over the tiles
     uint8_t* v_fp8;
     NormRopeArgs nr;
 };
@@ -56,7 +58,7 @@ struct PrepassArgs {
     const uint16_t* k; int64_t k_sb, k_sn, k_sh;
     const uint16_t* v; int64_t v_sb, v_sn, v_sh;
     int8_t* q_i8; float* q_scale;
-    int8_t* k_i8; float* k_scale; float* k_mean;
+    int8_t* k_i8; float* k_scale; float* k_mean; float* k_scale_max;
     uint8_t* v_fp8; float* v_scale;
     float* k_tile_sum; float* v_tile_amax; float* v_inv;
     bool norm_rope;      // apply the RMSNorm + RoPE producer to Q and K first
@@ -68,7 +70,7 @@ constexpr int kMainloopWaves = 4;
 
 struct MainloopArgs {
     const int8_t* q_i8; const float* q_scale;
-    const int8_t* k_i8; const float* k_scale;
+    const int8_t* k_i8; const float* k_scale; const float* k_scale_max;
     const uint8_t* v_fp8; const float* v_scale;
     const uint16_t* q_bf16; int64_t q_sb, q_sn, q_sh;  // non-null: quantize Q from BF16 here
     NormRopeArgs nr;     // nr.q_weight non-null: RMSNorm + RoPE the BF16 Q rows first

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(sage):
     lib = ctypes.CDLL(sage.library_path())
     missing = [n for n in _declared_functions() if not hasattr(lib, n)]
     assert missing == []
-    assert sage._load().sage_abi_version() == 2
+    assert sage._load().sage_abi_version() == 3
 
 
 def test_workspace_bytes(sage):
@@ -65,11 +65,12 @@ def test_carve_layout(sage):
     base = 0x7f0000000000                           # never dereferenced: carving is host arithmetic
     assert lib.sage_quantized_carve(shape, base, need, ctypes.byref(qz)) == 0
     ptrs = [qz.q_i8, qz.q_scale, qz.k_i8, qz.k_scale, qz.k_mean, qz.v_fp8, qz.v_scale,
-            qz.k_tile_sum, qz.v_tile_amax, qz.v_inv]
+            qz.k_tile_sum, qz.v_tile_amax, qz.v_inv, qz.k_scale_max]
     assert all(p % 256 == 0 for p in ptrs)
     assert ptrs == sorted(ptrs) and ptrs[0] == base
     sizes = [2 * 3 * 256 * 128, 2 * 3 * 8 * 4, 2 * 3 * 256 * 128, 2 * 3 * 4 * 4, 2 * 3 * 128 * 4,
-             2 * 3 * 256 * 128, 2 * 3 * 128 * 4, 2 * 3 * 4 * 128 * 4, 2 * 3 * 4 * 128 * 4, 2 * 3 * 128 * 4]
+             2 * 3 * 256 * 128, 2 * 3 * 128 * 4, 2 * 3 * 4 * 128 * 4, 2 * 3 * 4 * 128 * 4, 2 * 3 * 128 * 4,
+             2 * 3 * 4]
     for p, q, s in zip(ptrs, ptrs[1:] + [base + need], sizes):
         assert q - p >= s                              # regions do not overlap
     assert base + need - ptrs[-1] >= sizes[-1]

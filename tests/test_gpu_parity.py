@@ -153,6 +153,7 @@ def test_quantized_bytes_bit_exact(sage, name):
     assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
     assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
     assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.k_scale_max.cpu().numpy()), _bits(ref.k_scale.max(-1)))
     assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
     gq = layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N)
     assert np.array_equal(gq, ref.q_i8), "q_i8 differs in %d bytes" % int((gq != ref.q_i8).sum())
@@ -437,6 +438,7 @@ def test_batched_inputs_bit_exact_bytes_and_output(sage, layout):
     assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
     assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
     assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.k_scale_max.cpu().numpy()), _bits(ref.k_scale.max(-1)))
     assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
     assert np.array_equal(layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N), ref.q_i8)
     assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N), ref.k_i8)
@@ -498,6 +500,7 @@ def test_degenerate_operands_zero_scales(sage):
     torch.cuda.synchronize()
     ref = oracle.quantize(inp.q, k, v)
     assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.k_scale_max.cpu().numpy()), _bits(ref.k_scale.max(-1)))
     assert not np.any(ref.k_scale)
     assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
     assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), 1, 2, 300), ref.k_i8)
@@ -588,6 +591,7 @@ def test_long_sequence_one_head(sage):
     assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
     assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
     assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.k_scale_max.cpu().numpy()), _bits(ref.k_scale.max(-1)))
     assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
     assert np.array_equal(layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N), ref.q_i8)
     assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N), ref.k_i8)
