@@ -250,6 +250,28 @@ sage_status sage_attn_fwd_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k
                                     sage_shape s, const sage_norm_rope* nr, float sm_scale,
                                     const sage_bf16_out* o, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the device array the allocation-free entry point uses as its
+ * workspace (one array per GPU, held by the library until the process ends). */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sage_attn_fwd without a workspace argument.  Its workspace is a device
+ * array of SAGE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU; the
+ * call itself allocates nothing.  Shapes whose sage_workspace_bytes() exceed
+ * the array are rejected with SAGE_ERR_UNSUPPORTED before anything is
+ * launched (64 MiB holds, e.g., B=1, H=8, N=4096 or B=1, H=56, N=2048).  Every
+ * call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (nothing in it has to start at zero): calls whose kernels overlap
+ * on one GPU (on different streams, or from several host threads) race and
+ * give undefined output; calls on one stream are ordered and safe.  The first
+ * call on each device resolves the array's device address (a host query, no
+ * allocation); make that first call outside stream capture.  Output identical
+ * to sage_attn_fwd.  Errors: as sage_attn_fwd; UNSUPPORTED for a shape
+ * beyond the array; HIP when the array's address cannot be resolved. */
+sage_status sage_attn_fwd_noalloc(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                  sage_shape s, float sm_scale, const sage_bf16_out* o, void* stream);
+
 /* Static text for a status code. */
 const char* sage_status_string(sage_status st);
 

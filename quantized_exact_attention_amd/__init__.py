@@ -16,12 +16,13 @@ from . import build as _build
 
 __all__ = [
     "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv", "quantize_qkv_norm_rope",
-    "attn_fwd_quantized", "attn_fwd", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3",
+    "attn_fwd_quantized", "attn_fwd", "attn_fwd_noalloc", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3",
     "default_sm_scale",
 ]
 
 HEAD_DIM = 128
 ABI_VERSION = 3   # SAGE_ABI_VERSION of include/sage_mi355x.h that these structures follow
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SAGE_NOALLOC_SCRATCH_BYTES: the allocation-free path's workspace
 
 
 class SageError(RuntimeError):
@@ -95,6 +96,9 @@ def _load():
     lib.sage_attn_fwd.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.c_float, ctypes.POINTER(_Out),
                                                               P, ctypes.c_size_t, P]
     lib.sage_attn_fwd.restype = st
+    lib.sage_attn_fwd_noalloc.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.c_float,
+                                                                      ctypes.POINTER(_Out), P]
+    lib.sage_attn_fwd_noalloc.restype = st
     lib.sage_attn_fwd_norm_rope.argtypes = [ctypes.POINTER(_In)] * 3 + [_Shape, ctypes.POINTER(_NormRope),
                                                                         ctypes.c_float, ctypes.POINTER(_Out),
                                                                         P, ctypes.c_size_t, P]
@@ -339,6 +343,26 @@ def _one_call(q, k, v, sm_scale, out, workspace, nr):
 def attn_fwd(q, k, v, sm_scale: float = None, out=None, workspace=None):
     """Whole path (prepass + mainloop) in one call; returns BF16 [B, N, H, 128]."""
     return _one_call(q, k, v, sm_scale, out, workspace, None)
+
+
+def attn_fwd_noalloc(q, k, v, sm_scale: float = None, out=None):
+    """attn_fwd with the library's own fixed-size device workspace
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a caller workspace; the library
+    call allocates nothing (only `out`, when not given, is allocated here)."""
+    torch = _torch()
+    dq, dk, dv = _in_desc(q, "q"), _in_desc(k, "k"), _in_desc(v, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise SageError("q, k, v shapes differ")
+    B, N, H, _ = q.shape
+    if sm_scale is None:
+        sm_scale = default_sm_scale()
+    if out is None:
+        out = torch.empty((B, N, H, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    do = _out_desc(out, (B, N, H, HEAD_DIM))
+    _check(_load().sage_attn_fwd_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                         _Shape(B, N, H, HEAD_DIM), ctypes.c_float(sm_scale), ctypes.byref(do),
+                                         _stream_ptr(q)))
+    return out
 
 
 def attn_fwd_norm_rope(q, k, v, q_weight, k_weight, cos, sin, eps: float = 1e-6, sm_scale: float = None,

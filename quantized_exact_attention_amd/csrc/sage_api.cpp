@@ -321,6 +321,31 @@ sage_status sage_attn_fwd_norm_rope(const sage_bf16_in* q, const sage_bf16_in* k
     return one_call(q, k, v, s, nr, sm_scale, o, ws, ws_bytes, stream);
 }
 
+sage_status sage_attn_fwd_noalloc(const sage_bf16_in* q, const sage_bf16_in* k, const sage_bf16_in* v,
+                                  sage_shape s, float sm_scale, const sage_bf16_out* o, void* stream) {
+    clear_err();
+    Dims d;
+    if (!dims_of(s, &d))
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "invalid shape B=%d N=%d H=%d D=%d (need D=128, 1<=N<=2^24, B,H>=1, B*H<=2^24, B*H*2*ceil(N/128)<2^31)",
+                    s.B, s.N, s.H, s.D);
+    const size_t need = total_bytes(d);
+    if (need > SAGE_NOALLOC_SCRATCH_BYTES)
+        return fail(SAGE_ERR_UNSUPPORTED,
+                    "shape B=%d N=%d H=%d needs %zu workspace bytes; the allocation-free path holds %zu "
+                    "(use sage_attn_fwd with a caller workspace)",
+                    s.B, s.N, s.H, need, (size_t)SAGE_NOALLOC_SCRATCH_BYTES);
+    sage_status st;
+    if ((st = check_in(q, "q")) != SAGE_OK) return st;
+    if ((st = check_in(k, "k")) != SAGE_OK) return st;
+    if ((st = check_in(v, "v")) != SAGE_OK) return st;
+    if ((st = check_out(o)) != SAGE_OK) return st;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+        return fail(SAGE_ERR_INVALID_ARGUMENT, "sm_scale must be finite and > 0");
+    void* ws = nullptr;
+    if ((st = hip_status(sage::noalloc_scratch(&ws), "allocation-free workspace address")) != SAGE_OK) return st;
+    return one_call(q, k, v, s, nullptr, sm_scale, o, ws, need, stream);
+}
+
 sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* stream) {
     clear_err();
     Dims d;

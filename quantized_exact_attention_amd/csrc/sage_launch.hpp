@@ -96,4 +96,8 @@ hipError_t launch_mainloop(const MainloopArgs& p, hipStream_t stream);
 hipError_t launch_debug_qk(const DebugQkArgs& p, hipStream_t stream);
 hipError_t launch_cvt_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t stream);
 
+// Device address of this device's allocation-free workspace array
+// (sage_noalloc.hip): resolved on the first call per device, then cached.
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace sage

@@ -135,6 +135,33 @@ def test_validation_happens_before_launch(sage):
     assert lib.sage_status_string(3) == b"workspace missing, misaligned or too small"
 
 
+def test_noalloc_validation_happens_before_any_device_call(sage):
+    """The allocation-free entry point checks the shape against its fixed
+    workspace array, and its arguments, before it touches a device (these
+    calls run on a machine without a GPU)."""
+    lib = sage._load()
+    B = ctypes.byref
+    good = sage._In(0x7e0000000000, 200 * 2 * 128, 2 * 128, 128)
+    out_good = sage._Out(0x7d0000000000, 200 * 256, 256, 128)
+    small = sage._Shape(1, 200, 2, 128)
+    assert lib.sage_workspace_bytes(small) <= sage.NOALLOC_SCRATCH_BYTES
+    # the array holds a 4096-token, 8-head case but not the long-context one
+    assert lib.sage_workspace_bytes(sage._Shape(1, 4096, 8, 128)) <= sage.NOALLOC_SCRATCH_BYTES
+    big = sage._Shape(1, 37810, 56, 128)
+    assert lib.sage_workspace_bytes(big) > sage.NOALLOC_SCRATCH_BYTES
+    st = lib.sage_attn_fwd_noalloc(B(good), B(good), B(good), big, ctypes.c_float(0.088), B(out_good), None)
+    assert st == 2
+    msg = lib.sage_last_error_message().decode()
+    assert "allocation-free" in msg and str(sage.NOALLOC_SCRATCH_BYTES) in msg
+    assert lib.sage_attn_fwd_noalloc(B(good), B(good), B(good), sage._Shape(1, 200, 2, 64), ctypes.c_float(0.088),
+                                     B(out_good), None) == 1
+    assert lib.sage_attn_fwd_noalloc(B(sage._In(None, 0, 0, 0)), B(good), B(good), small, ctypes.c_float(0.088),
+                                     B(out_good), None) == 1
+    assert lib.sage_attn_fwd_noalloc(B(good), B(good), B(good), small, ctypes.c_float(0.0), B(out_good), None) == 1
+    assert lib.sage_attn_fwd_noalloc(B(good), B(good), B(good), small, ctypes.c_float(0.088),
+                                     B(sage._Out(None, 0, 0, 0)), None) == 1
+
+
 def test_layout_unpack_roundtrip():
     """The test-side unpackers are bijections onto the logical index space."""
     B, H, N = 1, 2, 200
