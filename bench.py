@@ -23,9 +23,15 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
               active shares and the matrix ops per active cycle (at the clock
               the chip actually ran) from profiles/mainloop_canonical_counters.md,
               under the same condition
-  cpu_baseline the CPU oracle on a bounded sample of the same workload
-              (one head's prepass plus whole query rows of that head over
-              all keys), extrapolated to the full workload
+  roofline_vector  the mainloop against its measured vector floor: cycles per
+              wave tile of the contract's per-score vector work (and of that
+              work plus the tile's matrix instructions) at three waves per
+              SIMD, times the tiles per SIMD, at the clock measured under that
+              load; frac = that floor with the matrix work / the mainloop time
+  cpu_baseline the CPU oracle on the host cores: the prepass of the whole
+              workload in full, whole query rows of one head over all keys
+              extrapolated to every row and head, and the 4096-token,
+              8-head mainloop in full
 """
 import argparse
 import hashlib
@@ -110,21 +116,76 @@ def prepass_bytes(B, N, H):
     return reads + writes
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
-    """Time the oracle on one head: its prepass over all N rows, then whole
-    query rows (all N keys each) in batches until min_seconds have passed."""
-    import numpy as np
+def vector_roofline(sage, dev, stream, w, mainloop_ms):
+    """The mainloop's vector floor, measured on this GPU: the shader clock
+    cycles one SIMD spends on one 32-query x 64-key wave tile of the
+    contract's per-score vector work alone, and with the tile's 12 matrix
+    instructions after it, at the mainloop's three waves per SIMD
+    (sage_debug_issue_probe on one CU), times the wave tiles each SIMD runs
+    for this workload, at the clock the chip holds under that load (cycle
+    counter over HIP-event time with every CU running it)."""
     import torch
+    wps, iters = 3, 4000
+    cycles = {}
+    for kind in (0, 1):
+        t = sage.debug_issue_probe(kind, wps, 1, iters, dev)
+        torch.cuda.synchronize(dev)
+        cycles[kind] = float(t.max().item()) / (iters * wps)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t = sage.debug_issue_probe(1, wps, cus, 8000, dev)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    clock = float(t.max().item()) / (e0.elapsed_time(e1) * 1e-3)
+    tiles = w.B * w.H * -(-w.N // 32) * -(-w.N // 64) / (4.0 * cus)
+    floor_v = cycles[0] * tiles / clock * 1e3
+    floor_vm = cycles[1] * tiles / clock * 1e3
+    return {"bound": "valu", "unit": "ms", "cycles_per_tile_vector": cycles[0],
+            "cycles_per_tile_vector_matrix": cycles[1], "clock_ghz": clock / 1e9, "tiles_per_simd": tiles,
+            "floor_ms": floor_v, "floor_with_matrix_ms": floor_vm, "achieved_ms": mainloop_ms,
+            "frac": floor_vm / mainloop_ms}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(w, inp, min_seconds=10.0, max_seconds=30.0):
+    """Time the oracle on the host cores: the prepass over the whole workload
+    (every head, in full), the mainloop of the 4096-token, 8-head workload in
+    full, and, for the whole workload's mainloop, whole query rows (all N keys
+    each) of head 0 in batches until min_seconds have passed, extrapolated to
+    every row of every head (rows cost the same in every head)."""
+    import numpy as np
 
     import oracle
     import workloads
 
-    one = workloads.Workload("sample", 1, w.N, 1, seed=w.seed, layout="projection")
-    inp = workloads.generate(one)
     threads = oracle.max_threads()
     t0 = time.perf_counter()
     qz = oracle.quantize(inp.q, inp.k, inp.v)
     t_prep = time.perf_counter() - t0
+
+    mw = workloads.by_name("mid")
+    mi = workloads.generate(mw)
+    mq = oracle.quantize(mi.q, mi.k, mi.v)
+    bb, hh, rr = np.meshgrid(np.arange(mw.B), np.arange(mw.H), np.arange(mw.N), indexing="ij")
+    t0 = time.perf_counter()
+    oracle.attn_rows(mq, np.stack([bb.ravel(), hh.ravel(), rr.ravel()], axis=1))
+    t_mid = time.perf_counter() - t0
+    del mi, mq
+
     rng = np.random.default_rng(0)
     rows_done = 0
     t_rows = 0.0
@@ -140,16 +201,24 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
         if dt < 2.0:
             batch *= 2
     per_row = t_rows / rows_done
-    est = w.B * w.H * (t_prep + per_row * w.N)
-    del torch
+    t_main = w.B * w.H * w.N * per_row
+    est = t_prep + t_main
     return {
         "value": effective_ops(w.B, w.N, w.H) / est / 1e12,
         "unit": "TOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": ("head 0 of the same workload: prepass over all %d rows (%.2f s) and %d whole query rows "
-                   "against all %d keys (%.2f s); extrapolated x%d heads to %.0f s for one step"
-                   % (w.N, t_prep, rows_done, w.N, t_rows, w.H, est)),
+        "cpu_model": cpu_model(),
+        "extrapolated": True,
+        "sample": ("prepass over the whole workload in full (%.2f s); mainloop: %d whole query rows of head 0 "
+                   "against all %d keys (%.2f s), extrapolated to all %d rows of %d heads (%.0f s); one step "
+                   "%.0f s.  Also in full: the mainloop of the 4096-token, 8-head workload, %.2f s (%.4f TOPS)"
+                   % (t_prep, rows_done, w.N, t_rows, w.N, w.B * w.H, t_main, est, t_mid,
+                      effective_ops(mw.B, mw.N, mw.H) / t_mid / 1e12)),
+        "prepass_full_s": t_prep,
+        "mainloop_extrapolated_s": t_main,
+        "mid_mainloop_full_s": t_mid,
+        "mid_mainloop_tops": effective_ops(mw.B, mw.N, mw.H) / t_mid / 1e12,
         "est_step_s": est,
     }
 
@@ -194,7 +263,8 @@ def main():
     else:
         buf = None
         qkv = [(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev))]
-    del inp
+    if args.no_cpu_baseline:
+        del inp          # the CPU oracle leg reads the same host inputs
     # Steps rotate over several copies of the inputs and of the quantized
     # operands (each set larger than the 256 MB Infinity Cache), so no call
     # finds its operands cached by the previous one.
@@ -342,10 +412,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
         "mainloop_pipes": recorded_pipes(w.name),
+        "roofline_vector": vector_roofline(sage, dev, stream, w, main_avg),
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        cb = cpu_baseline(w)
+        cb = cpu_baseline(w, inp)
         cb.pop("est_step_s")
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

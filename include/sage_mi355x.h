@@ -293,6 +293,26 @@ sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* st
  * values; |x| must be below 464 for a finite code.  Errors: INVALID_ARGUMENT, HIP. */
 sage_status sage_debug_cvt_e4m3(const float* x, uint8_t* y, int64_t n, void* stream);
 
+/* Shader clock cycles of the mainloop's tile step on this GPU (the vector
+ * roofline the benchmark reports next to the matrix one).  Launches `blocks`
+ * workgroups of 4*waves_per_simd waves (waves_per_simd waves on each SIMD of a
+ * CU); every wave runs `iters` repetitions of one instruction stream and
+ * stores the cycles it took (s_memtime difference) at
+ * ticks[block * 4*waves_per_simd + wave] (device memory, blocks *
+ * 4*waves_per_simd entries).  The streams (kind):
+ *   0  the vector work of one 32-query x 64-key wave tile under the
+ *      contract's per-score arithmetic, fused score form (160 instructions:
+ *      32 float(S) subtractions, 32 score FMAs, 32 exp2, 32 denominator adds,
+ *      16 E4M3 pair conversions, 16 three-input maxima), no memory access
+ *   1  stream 0 followed by the tile's matrix work in one burst (4 FP8
+ *      32x32x64 and 8 INT8 32x32x32 instructions)
+ *   2  the 12 matrix instructions alone
+ * A SIMD's cycles per tile = the largest count among its waves /
+ * (iters * waves_per_simd).  1 <= waves_per_simd <= 4, 1 <= blocks <= 65536,
+ * 1 <= iters <= 2^20.  Errors: INVALID_ARGUMENT, HIP. */
+sage_status sage_debug_issue_probe(int32_t kind, int32_t waves_per_simd, int32_t blocks, int32_t iters,
+                                   uint64_t* ticks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

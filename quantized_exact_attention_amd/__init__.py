@@ -16,7 +16,7 @@ from . import build as _build
 
 __all__ = [
     "SageError", "library_path", "workspace_bytes", "Quantized", "quantize_qkv", "quantize_qkv_norm_rope",
-    "attn_fwd_quantized", "attn_fwd", "attn_fwd_noalloc", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3",
+    "attn_fwd_quantized", "attn_fwd", "attn_fwd_noalloc", "attn_fwd_norm_rope", "debug_qk_s32", "debug_cvt_e4m3", "debug_issue_probe",
     "default_sm_scale",
 ]
 
@@ -112,6 +112,8 @@ def _load():
     lib.sage_debug_qk_s32.restype = st
     lib.sage_debug_cvt_e4m3.argtypes = [P, P, ctypes.c_int64, P]
     lib.sage_debug_cvt_e4m3.restype = st
+    lib.sage_debug_issue_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.sage_debug_issue_probe.restype = st
     if lib.sage_abi_version() != ABI_VERSION:
         raise SageError("%s has ABI version %d, this binding needs %d (rebuild the library)"
                         % (_build.LIB, lib.sage_abi_version(), ABI_VERSION))
@@ -381,6 +383,16 @@ def debug_qk_s32(qz: Quantized):
     s = torch.empty((qz.B, qz.H, qz.Nq, qz.T * 64), dtype=torch.int32, device=qz.device)
     _check(_load().sage_debug_qk_s32(ctypes.byref(qz.c), s.data_ptr(), _stream_ptr(s)))
     return s
+
+
+def debug_issue_probe(kind: int, waves_per_simd: int, blocks: int, iters: int, device=None):
+    """Cycle counts of the mainloop's tile-step instruction streams
+    (sage_debug_issue_probe): an int64 GPU tensor [blocks, 4*waves_per_simd]."""
+    torch = _torch()
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    ticks = torch.zeros((blocks, 4 * waves_per_simd), dtype=torch.int64, device=device)
+    _check(_load().sage_debug_issue_probe(kind, waves_per_simd, blocks, iters, ticks.data_ptr(), _stream_ptr(ticks)))
+    return ticks
 
 
 def debug_cvt_e4m3(x):

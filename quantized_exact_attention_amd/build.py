@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsage_mi355x.so")
-SOURCES = ["prep_kernels.hip", "attn_mainloop.hip", "sage_noalloc.hip", "sage_api.cpp"]
+SOURCES = ["prep_kernels.hip", "attn_mainloop.hip", "sage_noalloc.hip", "issue_probe.hip", "sage_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # What the mainloop kernel may use: registers for three waves per SIMD.

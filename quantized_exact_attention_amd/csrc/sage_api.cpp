@@ -369,4 +369,16 @@ sage_status sage_debug_cvt_e4m3(const float* x, uint8_t* y, int64_t n, void* str
     return hip_status(sage::launch_cvt_e4m3(x, y, n, (hipStream_t)stream), "cvt launch");
 }
 
+sage_status sage_debug_issue_probe(int32_t kind, int32_t waves_per_simd, int32_t blocks, int32_t iters,
+                                   uint64_t* ticks, void* stream) {
+    clear_err();
+    if (kind < 0 || kind > 2) return fail(SAGE_ERR_INVALID_ARGUMENT, "kind must be 0, 1 or 2");
+    if (waves_per_simd < 1 || waves_per_simd > 4) return fail(SAGE_ERR_INVALID_ARGUMENT, "waves_per_simd must be 1..4");
+    if (blocks < 1 || blocks > 65536) return fail(SAGE_ERR_INVALID_ARGUMENT, "blocks must be 1..65536");
+    if (iters < 1 || iters > (1 << 20)) return fail(SAGE_ERR_INVALID_ARGUMENT, "iters must be 1..2^20");
+    if (!ticks) return fail(SAGE_ERR_INVALID_ARGUMENT, "ticks is NULL");
+    return hip_status(sage::launch_issue_probe(kind, waves_per_simd, blocks, iters, ticks, (hipStream_t)stream),
+                      "issue probe launch");
+}
+
 }  // extern "C"

@@ -96,6 +96,11 @@ hipError_t launch_mainloop(const MainloopArgs& p, hipStream_t stream);
 hipError_t launch_debug_qk(const DebugQkArgs& p, hipStream_t stream);
 hipError_t launch_cvt_e4m3(const float* x, uint8_t* y, int64_t n, hipStream_t stream);
 
+// Instruction streams of the issue probe (issue_probe.hip).
+enum IssueProbeKind { kIssueMix = 0, kIssueMixMfma = 1, kIssueMfma = 2 };
+hipError_t launch_issue_probe(int kind, int waves_per_simd, int blocks, int iters, uint64_t* ticks,
+                              hipStream_t stream);
+
 // Device address of this device's allocation-free workspace array
 // (sage_noalloc.hip): resolved on the first call per device, then cached.
 hipError_t noalloc_scratch(void** out);

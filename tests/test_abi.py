@@ -133,6 +133,9 @@ def test_validation_happens_before_launch(sage):
     assert lib.sage_debug_cvt_e4m3(0x1000, 0x1000, -1, None) == 1
     assert lib.sage_debug_cvt_e4m3(0x1000, 0x1000, 0, None) == 0                # empty: nothing to do
     assert lib.sage_status_string(3) == b"workspace missing, misaligned or too small"
+    for kind, wps, blocks, iters, ptr in [(3, 3, 1, 10, 0x1000), (0, 0, 1, 10, 0x1000), (0, 5, 1, 10, 0x1000),
+                                          (0, 3, 0, 10, 0x1000), (0, 3, 1, 0, 0x1000), (0, 3, 1, 10, None)]:
+        assert lib.sage_debug_issue_probe(kind, wps, blocks, iters, ptr, None) == 1
 
 
 def test_noalloc_validation_happens_before_any_device_call(sage):
