@@ -50,15 +50,6 @@ constexpr float kLog2Of448 = 8.8073549220576041f;  // log2(448)
 // Scheduling fence: the compiler moves no instruction across it.
 #define SAGE_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Bijection from dispatch order to work items such that the items dispatched
-// to one XCD (dispatch index mod 8) are consecutive.
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-    const int q = nwg >> 3, r = nwg & 7;
-    const int xcd = wg & 7, slot = wg >> 3;
-    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-    return base + slot;
-}
-
 // Score accumulators start at the bit pattern of 1.5 * 2^23 instead of 0.
 // Every |S| <= 128 * 127 * 127 < 2^22, so the int32 result 0x4B400000 + S is
 // the FP32 number 1.5 * 2^23 + S (fixed exponent, S in the mantissa): one

@@ -69,6 +69,16 @@ __global__ __launch_bounds__(256) void tile_stats_kernel(StatsArgs a) {
 
 constexpr int kVRow = kHD + 8;   // LDS row pitch in BF16 elements (272 bytes)
 
+// The RMSNorm + RoPE kernels take their (b, h, tile) items tile-major with
+// (b, h) minor, through the XCD remap: each XCD then works through its own
+// range of tiles with every head of a tile in flight together, so the tile's
+// 64 angle rows (32 KiB) come from HBM once per XCD instead of once per head.
+__device__ __forceinline__ void tile_major_item(const int BH, int& bh, int& t) {
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    t = u / BH;
+    bh = u - t * BH;
+}
+
 // tile_stats with the RMSNorm + RoPE producer applied to K: one block of 256
 // threads per (b, h, 64-row tile).  Waves 0-1 load 32 K rows each in the QK
 // operand split, normalise and rotate them (norm_rope_row) and stage the BF16
@@ -79,9 +89,8 @@ constexpr int kVRow = kHD + 8;   // LDS row pitch in BF16 elements (272 bytes)
 __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
     __shared__ uint16_t tile[kBK * kVRow];
     __shared__ float vam[8][kHD];
-    const int64_t blk = blockIdx.x;
-    const int bh = (int)(blk / a.T);
-    const int t = (int)(blk % a.T);
+    int bh, t;
+    tile_major_item(a.BH, bh, t);
     const int b = bh / a.H, h = bh % a.H;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -222,9 +231,14 @@ template <bool kNormRope>
 __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
     __shared__ uint16_t tile[kBK * kVRow];
     __shared__ float k_amax[2];
-    const int64_t blk = blockIdx.x;
-    const int bh = (int)(blk / a.Tq);
-    const int t = (int)(blk % a.Tq);
+    int bh, t;
+    if constexpr (kNormRope) {
+        tile_major_item(a.BH, bh, t);
+    } else {
+        const int64_t blk = blockIdx.x;
+        bh = (int)(blk / a.Tq);
+        t = (int)(blk % a.Tq);
+    }
     const int b = bh / a.H, h = bh % a.H;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -390,7 +404,7 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         StatsArgs a;
         a.k = p.k; a.k_sb = p.k_sb; a.k_sn = p.k_sn; a.k_sh = p.k_sh;
         a.v = p.v; a.v_sb = p.v_sb; a.v_sn = p.v_sn; a.v_sh = p.v_sh;
-        a.H = p.H; a.N = p.N; a.T = p.T; a.units = BH * p.T;
+        a.H = p.H; a.N = p.N; a.T = p.T; a.BH = (int)BH; a.units = BH * p.T;
         a.k_tile_sum = p.k_tile_sum; a.v_tile_amax = p.v_tile_amax;
         a.nr = p.nr;
         if (p.norm_rope) {
@@ -412,7 +426,7 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         a.q = p.with_q ? p.q : nullptr; a.q_sb = p.q_sb; a.q_sn = p.q_sn; a.q_sh = p.q_sh;
         a.k = p.k; a.k_sb = p.k_sb; a.k_sn = p.k_sn; a.k_sh = p.k_sh;
         a.v = p.v; a.v_sb = p.v_sb; a.v_sn = p.v_sn; a.v_sh = p.v_sh;
-        a.H = p.H; a.N = p.N; a.T = p.T; a.G = p.G;
+        a.H = p.H; a.N = p.N; a.T = p.T; a.G = p.G; a.BH = (int)BH;
         a.Tq = p.with_q ? p.G / 2 : p.T;
         a.k_mean = p.k_mean; a.v_inv = p.v_inv; a.v_scale = p.v_scale;
         a.q_i8 = p.q_i8; a.q_scale = p.q_scale; a.k_i8 = p.k_i8; a.k_scale = p.k_scale; a.v_fp8 = p.v_fp8;

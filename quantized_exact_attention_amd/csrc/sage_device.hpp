@@ -150,6 +150,15 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, t);
 }
 
+// Bijection from dispatch order to work items such that the items dispatched
+// to one XCD (dispatch index mod 8; each XCD has its own L2) are consecutive.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+    const int q = nwg >> 3, r = nwg & 7;
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return base + slot;
+}
+
 __device__ __forceinline__ uint32_t& word_of(uint4& w, int m) {
     return m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w;
 }

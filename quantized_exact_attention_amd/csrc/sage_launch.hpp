@@ -19,6 +19,7 @@ struct StatsArgs {
     const uint16_t* k; int64_t k_sb, k_sn, k_sh;
     const uint16_t* v; int64_t v_sb, v_sn, v_sh;
     int H, N, T;
+    int BH;              // B * H
     int64_t units;
     float* k_tile_sum;
     float* v_tile_amax;
@@ -40,6 +41,7 @@ struct QuantArgs {
     const uint16_t* k; int64_t k_sb, k_sn, k_sh;
     const uint16_t* v; int64_t v_sb, v_sn, v_sh;
     int H, N, T, G;
+    int BH;              // B * H
     int Tq;              // 64-row tiles per (b, h) this launch covers (>= T)
     const float* k_mean;
     const float* v_inv;
