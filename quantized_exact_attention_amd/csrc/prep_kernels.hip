@@ -16,15 +16,16 @@
 // Launch sequence (one stream):
 //   1. tile_stats    per 64-row tile: FP32 in-order channel sums of K and
 //                    channel absolute maxima of V          (reads K, V)
-//                    (tile_stats_nr when the optional RMSNorm + RoPE
-//                    producer is applied to Q and K: the normalised rows are
-//                    recomputed in launches 1 and 3 and never stored)
 //   2. finalize      per (b,h): k_mean from the tile sums in tile order; V
 //                    channel amax, v_scale = a/448, v_inv = 448/a
 //   3. quant_qkv     per 64-row tile, one pass over its Q, K and V rows:
 //                    INT8 Q per 32-row group, INT8 K - k_mean per tile,
 //                    E4M3 V in the mainloop's layout (Q is skipped when the
 //                    mainloop quantizes it itself)
+// With the optional RMSNorm + RoPE producer on Q and K, launch 1 is
+// tile_stats_nr, which also normalises and quantizes Q (needing neither
+// k_mean nor the V scales), and launch 3 is quant_kv_nr: the normalised K
+// rows are recomputed in launches 1 and 3 and never stored.
 #include "sage_device.hpp"
 #include "sage_launch.hpp"
 
@@ -69,45 +70,65 @@ __global__ __launch_bounds__(256) void tile_stats_kernel(StatsArgs a) {
 
 constexpr int kVRow = kHD + 8;   // LDS row pitch in BF16 elements (272 bytes)
 
-// The RMSNorm + RoPE kernels take their (b, h, tile) items tile-major with
-// (b, h) minor, through the XCD remap: each XCD then works through its own
-// range of tiles with every head of a tile in flight together, so the tile's
-// 64 angle rows (32 KiB) come from HBM once per XCD instead of once per head.
-__device__ __forceinline__ void tile_major_item(const int BH, int& bh, int& t) {
+// The RMSNorm + RoPE kernels give each block two heads (bh0 and bh0 + 1) of
+// one 64-row tile, so that all four waves do the same normalisation work, and
+// take these items tile-major with the head pairs minor, through the XCD
+// remap: each XCD then works through its own range of tiles with every head
+// of a tile in flight together, so the tile's 64 angle rows (32 KiB) come
+// from HBM once per XCD instead of once per head.
+__device__ __forceinline__ void pair_item(int BH, int& t, int& bh0) {
+    const int pairs = (BH + 1) >> 1;
     const int u = xcd_remap(blockIdx.x, gridDim.x);
-    t = u / BH;
-    bh = u - t * BH;
+    t = u / pairs;
+    bh0 = 2 * (u - t * pairs);
 }
 
-// tile_stats with the RMSNorm + RoPE producer applied to K: one block of 256
-// threads per (b, h, 64-row tile).  Waves 0-1 load 32 K rows each in the QK
-// operand split, normalise and rotate them (norm_rope_row) and stage the BF16
-// results in LDS; waves 2-3 take channel absolute maxima of V (thread u owns
-// channels 8*(u%16)..+7 of rows u/16, u/16 + 8, ...).  Then thread d sums
-// channel d of the staged rows in row order and threads 128+d combine the
-// eight V partial maxima of channel d.
+// One row of 128 BF16 channels of the lane's share in the QK operand split
+// (lane l: row l%32, channels 32kk + 16*(l/32) + 0..15 in w[2kk], w[2kk+1]);
+// rows that are not valid read as zeros.
+__device__ __forceinline__ void load_row_words(const uint16_t* p, bool valid, uint4 (&w)[8]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        w[2 * kk] = valid ? *(const uint4*)(p + 32 * kk) : make_uint4(0, 0, 0, 0);
+        w[2 * kk + 1] = valid ? *(const uint4*)(p + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// tile_stats with the RMSNorm + RoPE producer.  Wave w serves head bh0 + w/2
+// and rows 32*(w%2) .. +31 of tile t:
+//   * it loads those K rows, normalises and rotates them (norm_rope_row) and
+//     stages the BF16 results in LDS;
+//   * lane (c8 = l%16, rp = l/16) takes the absolute maxima of V channels
+//     8c8 .. 8c8+7 over its rows rp, rp+4, ..., rp+28 of the wave's 32; the
+//     four lanes of one c8 combine across the wave and leave the wave's 128
+//     channel maxima in LDS;
+//   * when Q is quantized in this pass, it does the same normalisation for
+//     Q group 2t + w%2 of its head and writes that group's INT8 codes and
+//     scale (blocks past the last K/V tile, t >= T, do only this: the Q
+//     padding reaches 64 * G/2 >= 64 * T rows).
+// Then thread (s = u/128, d = u%128) sums channel d of head bh0 + s's staged
+// rows in row order and combines the two halves' V maxima of channel d.
 __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
-    __shared__ uint16_t tile[kBK * kVRow];
-    __shared__ float vam[8][kHD];
-    int bh, t;
-    tile_major_item(a.BH, bh, t);
-    const int b = bh / a.H, h = bh % a.H;
+    __shared__ uint16_t tile[2][kBK * kVRow];
+    __shared__ float vam[2][2][kHD];
+    int t, bh0;
+    pair_item(a.BH, t, bh0);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int hs = wave >> 1, half = wave & 1;
+    const int bh = bh0 + hs;
+    const bool head = bh < a.BH;     // uniform per wave
+    const int b = bh / a.H, h = bh - b * a.H;
+    const bool kv = t < a.T;         // uniform per block
     const int n0 = t * kBK;
-    const int rows = min(kBK, a.N - n0);
-    if (wave < 2) {
-        const int hf = lane >> 5;
-        const int row = 32 * wave + (lane & 31);
+    const int hf = lane >> 5;
+    if (kv && head) {
+        const int rows = min(kBK, a.N - n0);
+        const int row = 32 * half + (lane & 31);
         const int n = n0 + row;
         const bool valid = row < rows;
-        const uint16_t* kp = a.k + b * a.k_sb + (int64_t)n * a.k_sn + h * a.k_sh + 16 * hf;
         uint4 w[8];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            w[2 * kk] = valid ? *(const uint4*)(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
-            w[2 * kk + 1] = valid ? *(const uint4*)(kp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
-        }
+        load_row_words(a.k + b * a.k_sb + (int64_t)n * a.k_sn + h * a.k_sh + 16 * hf, valid, w);
         const int na = valid ? n : 0;
         norm_rope_row(w, hf, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
                       a.nr.eps);
@@ -115,49 +136,70 @@ __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                *(uint4*)(&tile[row * kVRow + 32 * kk + 16 * hf + 8 * e]) = w[2 * kk + e];
-    } else {
-        const int u = threadIdx.x - 128;
-        const int c8 = u & 15;
-        const int rp = u >> 4;
+                *(uint4*)(&tile[hs][row * kVRow + 32 * kk + 16 * hf + 8 * e]) = w[2 * kk + e];
+
+        const int c8 = lane & 15, rp = lane >> 4;
         const uint16_t* vp = a.v + b * a.v_sb + h * a.v_sh + 8 * c8;
         float am[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am[i] = 0.0f;
+        for (int c = 0; c < 8; ++c) am[c] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int row = rp + 8 * i;
-            if (row < rows) {
+            const int r = 32 * half + rp + 4 * i;
+            if (r < rows) {
                 float vf[8];
-                unpack8(*(const uint4*)(vp + (int64_t)(n0 + row) * a.v_sn), vf);
+                unpack8(*(const uint4*)(vp + (int64_t)(n0 + r) * a.v_sn), vf);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) am[c] = fmaxf(am[c], fabsf(vf[c]));
             }
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) vam[rp][8 * c8 + c] = am[c];
-    }
-    __syncthreads();
-    const int d = threadIdx.x & 127;
-    if (threadIdx.x < 128) {
-        float sum = 0.0f;
-        if (rows == kBK) {
-            // all 64 LDS reads in flight before the ordered adds
-            float x[kBK];
-#pragma unroll
-            for (int row = 0; row < kBK; ++row) x[row] = bf16_bits_to_f32(tile[row * kVRow + d]);
-#pragma unroll
-            for (int row = 0; row < kBK; ++row) sum = sum + x[row];
-        } else {
-            for (int row = 0; row < rows; ++row) sum = sum + bf16_bits_to_f32(tile[row * kVRow + d]);
+        for (int c = 0; c < 8; ++c) {
+            am[c] = fmaxf(am[c], __shfl_xor(am[c], 16, 64));
+            am[c] = fmaxf(am[c], __shfl_xor(am[c], 32, 64));
         }
-        a.k_tile_sum[((int64_t)bh * a.T + t) * kHD + d] = sum;
-    } else {
-        float m = vam[0][d];
+        if (lane < 16) {
 #pragma unroll
-        for (int i = 1; i < 8; ++i) m = fmaxf(m, vam[i][d]);
-        a.v_tile_amax[((int64_t)bh * a.T + t) * kHD + d] = m;
+            for (int c = 0; c < 8; ++c) vam[hs][half][8 * c8 + c] = am[c];
+        }
     }
+    if (a.q != nullptr && head) {
+        const int g = 2 * t + half;
+        const int n = g * kQG + (lane & 31);
+        const bool valid = n < a.N;
+        uint4 w[8];
+        load_row_words(a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + 16 * hf, valid, w);
+        const int na = valid ? n : 0;
+        norm_rope_row(w, hf, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
+                      a.nr.eps);
+        uint4 codes[4];
+        const float scale = quant_q_words(w, codes);
+        int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
+        if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
+    }
+    if (!kv) return;                 // uniform per block: no wave reaches the barrier
+    __syncthreads();
+    const int sl = threadIdx.x >> 7, d = threadIdx.x & 127;
+    const int bhs = bh0 + sl;
+    if (bhs >= a.BH) return;
+    const int rows = min(kBK, a.N - n0);
+    const uint16_t* col = &tile[sl][d];
+    float sum = 0.0f;
+    if (rows == kBK) {
+        // all 64 LDS reads in flight before the ordered adds
+        float x[kBK];
+#pragma unroll
+        for (int row = 0; row < kBK; ++row) x[row] = bf16_bits_to_f32(col[row * kVRow]);
+#pragma unroll
+        for (int row = 0; row < kBK; ++row) sum = sum + x[row];
+    } else {
+        for (int row = 0; row < rows; ++row) sum = sum + bf16_bits_to_f32(col[row * kVRow]);
+    }
+    const int64_t o = ((int64_t)bhs * a.T + t) * kHD + d;
+    a.k_tile_sum[o] = sum;
+    a.v_tile_amax[o] = fmaxf(vam[sl][0][d], vam[sl][1][d]);
 }
 
 // One block of 128 threads per (b, h); thread d owns channel d.
@@ -214,161 +256,44 @@ __device__ __forceinline__ float k_row_amax(const uint4 (&kraw)[4][2], const flo
     return am;
 }
 
-// One block of 256 threads per (b, h, 64-row tile t) quantizes everything the
-// tile's rows hold, so each projection row segment is read once:
-//   waves 0, 1  Q groups 2t and 2t+1 (when Q is quantized here): lane l reads
-//               row 32g + l%32, channels 32kk + 16*(l/32) + 0..15, exactly the
-//               16 bytes it writes for kk
-//   waves 2, 3  K rows 64t + 32*(w-2) + l%32, same channel split; the tile's
-//               absolute maximum of K - k_mean is combined through LDS, then
-//               each wave writes the codes of its 32 rows
-//   all waves   the BF16 V tile is staged row-major in LDS; each 16-byte
-//               output chunk then gathers 16 rows of one channel in the PV
-//               operand order
-// Blocks past the last K/V tile (t >= T, only when Q is quantized: the Q
-// padding reaches 64*Tq >= 64*T rows) write the all-padding Q groups.
-template <bool kNormRope>
-__global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
-    __shared__ uint16_t tile[kBK * kVRow];
-    __shared__ float k_amax[2];
-    int bh, t;
-    if constexpr (kNormRope) {
-        tile_major_item(a.BH, bh, t);
-    } else {
-        const int64_t blk = blockIdx.x;
-        bh = (int)(blk / a.Tq);
-        t = (int)(blk % a.Tq);
+// INT8 codes of one wave's 32 K rows minus k_mean at scale am/127 (am: the
+// tile's absolute maximum of K - k_mean; below 2^-100 the scale is 0 and the
+// codes are zero), in the QK operand order of tile half `half`: lane l holds
+// row 32*half + l%32 as kraw (see k_row_amax); rows at or beyond N get zero
+// codes.  Returns the scale.
+__device__ __forceinline__ float k_codes(const uint4 (&kraw)[4][2], const float* kmp, float am, bool row_valid,
+                                         int8_t* tile_out, int half, int lane) {
+    float scale = 0.0f, inv = 0.0f;
+    if (am >= kAmaxFloor) {
+        scale = am / 127.0f;
+        inv = 127.0f / am;
     }
-    const int b = bh / a.H, h = bh % a.H;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const bool kv = t < a.T;   // uniform over the block
-
-    // V rows: thread (row, seg) loads 32 channels of one row.
-    const int vrow = threadIdx.x >> 2;
-    const int vseg = threadIdx.x & 3;
-    const int half = wave - 2;
-    const int c0 = 16 * (lane >> 5);
-    const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;
-    const int kn = t * kBK + 32 * half + (lane & 31);
-    uint4 kraw[4][2];
-    if constexpr (kNormRope) {
-        // This wave's Q or K row words are loaded first, then the V rows,
-        // which go to LDS at once so that no V registers stay live through
-        // the normalisation.
-        const bool do_q = wave < 2 && a.q != nullptr;
-        const bool do_k = wave >= 2 && kv;
-        const int g = 2 * t + wave;
-        const int n = do_q ? g * kQG + (lane & 31) : kn;
-        const bool valid = (do_q || do_k) && n < a.N;
-        const uint16_t* rp = do_q ? a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + c0
-                                  : a.k + b * a.k_sb + (int64_t)n * a.k_sn + h * a.k_sh + c0;
-        uint4 w[8];
+    int8_t* out = tile_out + lane * 16;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            w[2 * kk] = valid ? *(const uint4*)(rp + 32 * kk) : make_uint4(0, 0, 0, 0);
-            w[2 * kk + 1] = valid ? *(const uint4*)(rp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+        float x[16];
+        unpack8(kraw[kk][0], x);
+        unpack8(kraw[kk][1], x + 8);
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+            const v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
+            x[i] = x[i] - m4[0];
+            x[i + 1] = x[i + 1] - m4[1];
+            x[i + 2] = x[i + 2] - m4[2];
+            x[i + 3] = x[i + 3] - m4[3];
         }
-        if (kv) {
-            const int nv = t * kBK + vrow;
-            const uint16_t* vp = a.v + b * a.v_sb + (int64_t)nv * a.v_sn + h * a.v_sh + 32 * vseg;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *(uint4*)(&tile[vrow * kVRow + 32 * vseg + 8 * i]) =
-                    nv < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
-        }
-        if (do_q || do_k) {
-            const int na = valid ? n : 0;
-            norm_rope_row(w, lane >> 5, do_q ? a.nr.q_weight : a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2),
-                          a.nr.sin + (int64_t)na * (kHD / 2), a.nr.eps);
-        }
-        if (do_q) {
-            uint4 codes[4];
-            const float scale = quant_q_words(w, codes);
-            int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
-            if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
-        } else if (do_k) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) { kraw[kk][0] = w[2 * kk]; kraw[kk][1] = w[2 * kk + 1]; }
-            const float am = wave_max(valid ? k_row_amax(kraw, kmp) : 0.0f);
-            if (lane == 0) k_amax[half] = am;
-        }
-    } else {
-        uint4 vraw[4];
-        if (kv) {
-            const int n = t * kBK + vrow;
-            const uint16_t* vp = a.v + b * a.v_sb + (int64_t)n * a.v_sn + h * a.v_sh + 32 * vseg;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vraw[i] = n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
-        }
-        if (wave < 2) {
-            if (a.q != nullptr) {
-                const int g = 2 * t + wave;
-                const int n = g * kQG + (lane & 31);
-                const uint16_t* qp = a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + c0;
-                uint4 codes[4];
-                const float scale = quant_q_group(qp, n < a.N, codes);
-                int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
-                if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
-            }
-        } else if (kv) {
-            // this wave's share of the tile's absolute maximum of K - k_mean
-            const bool valid = kn < a.N;
-            const uint16_t* kp = a.k + b * a.k_sb + (int64_t)kn * a.k_sn + h * a.k_sh + c0;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                kraw[kk][0] = valid ? *(const uint4*)(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
-                kraw[kk][1] = valid ? *(const uint4*)(kp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
-            }
-            const float am = wave_max(valid ? k_row_amax(kraw, kmp) : 0.0f);
-            if (lane == 0) k_amax[half] = am;
-        }
-        if (kv) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *(uint4*)(&tile[vrow * kVRow + 32 * vseg + 8 * i]) = vraw[i];
-        }
+        uint4 codes = pack16_int8(x, inv);
+        if (!row_valid) codes = make_uint4(0, 0, 0, 0);
+        *(uint4*)(out + (half * 4 + kk) * 64 * 16) = codes;
     }
-    __syncthreads();
-    if (!kv) return;
+    return scale;
+}
 
-    if (wave >= 2) {
-        const float am = fmaxf(k_amax[0], k_amax[1]);
-        float scale = 0.0f, inv = 0.0f;
-        if (am >= kAmaxFloor) {
-            scale = am / 127.0f;
-            inv = 127.0f / am;
-        }
-        int8_t* out = a.k_i8 + ((int64_t)bh * a.T + t) * kTileBytes + lane * 16;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            float x[16];
-            unpack8(kraw[kk][0], x);
-            unpack8(kraw[kk][1], x + 8);
-#pragma unroll
-            for (int i = 0; i < 16; i += 4) {
-                const v4f m4 = *(const v4f*)(kmp + 32 * kk + i);
-                x[i] = x[i] - m4[0];
-                x[i + 1] = x[i + 1] - m4[1];
-                x[i + 2] = x[i + 2] - m4[2];
-                x[i + 3] = x[i + 3] - m4[3];
-            }
-            uint4 codes = pack16_int8(x, inv);
-            if (kn >= a.N) codes = make_uint4(0, 0, 0, 0);
-            *(uint4*)(out + (half * 4 + kk) * 64 * 16) = codes;
-        }
-        if (wave == 2 && lane == 0) {
-            a.k_scale[(int64_t)bh * a.T + t] = scale;
-            // the head's largest K scale: scales are >= 0, so their bit
-            // patterns order as the values do
-            atomicMax((unsigned int*)a.k_scale_max + bh, __float_as_uint(scale));
-        }
-    }
-
-    uint8_t* out = a.v_fp8 + ((int64_t)bh * a.T + t) * kTileBytes;
+// E4M3 codes of one BF16 V tile staged row-major in LDS (pitch kVRow), in
+// the PV operand order: each 16-byte output chunk gathers 16 rows of one
+// channel; the block's 256 threads write the tile's 512 chunks.
+__device__ __forceinline__ void v_codes(const uint16_t* tile, const float* v_inv, const float* v_scale,
+                                        uint8_t* out) {
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
         const int c = threadIdx.x + 256 * rep;          // 16-byte chunk index
@@ -377,8 +302,8 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
         const int l = c & 63;
         const int d = 32 * db + (l & 31);
         const int hh = l >> 5;
-        const float inv = a.v_inv[(int64_t)bh * kHD + d];
-        const bool zero = a.v_scale[(int64_t)bh * kHD + d] == 0.0f;
+        const float inv = v_inv[d];
+        const bool zero = v_scale[d] == 0.0f;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -396,10 +321,162 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
     }
 }
 
+// One block of 256 threads per (b, h, 64-row tile t) quantizes everything the
+// tile's rows hold, so each projection row segment is read once:
+//   waves 0, 1  Q groups 2t and 2t+1 (when Q is quantized here): lane l reads
+//               row 32g + l%32, channels 32kk + 16*(l/32) + 0..15, exactly
+//               the 16 bytes it writes for kk
+//   waves 2, 3  K rows 64t + 32*(w-2) + l%32, same channel split; the tile's
+//               absolute maximum of K - k_mean is combined through LDS, then
+//               each wave writes the codes of its 32 rows
+//   all waves   the BF16 V tile is staged row-major in LDS, then v_codes
+// Blocks past the last K/V tile (t >= T, only when Q is quantized: the Q
+// padding reaches 64*Tq >= 64*T rows) write the all-padding Q groups.
+__global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
+    __shared__ uint16_t tile[kBK * kVRow];
+    __shared__ float k_amax[2];
+    const int64_t blk = blockIdx.x;
+    const int bh = (int)(blk / a.Tq);
+    const int t = (int)(blk % a.Tq);
+    const int b = bh / a.H, h = bh % a.H;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const bool kv = t < a.T;   // uniform over the block
+
+    // V rows: thread (row, seg) loads 32 channels of one row.
+    const int vrow = threadIdx.x >> 2;
+    const int vseg = threadIdx.x & 3;
+    const int half = wave - 2;
+    const int c0 = 16 * (lane >> 5);
+    const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;
+    const int kn = t * kBK + 32 * half + (lane & 31);
+    uint4 kraw[4][2];
+    uint4 vraw[4];
+    if (kv) {
+        const int n = t * kBK + vrow;
+        const uint16_t* vp = a.v + b * a.v_sb + (int64_t)n * a.v_sn + h * a.v_sh + 32 * vseg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vraw[i] = n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
+    }
+    if (wave < 2) {
+        if (a.q != nullptr) {
+            const int g = 2 * t + wave;
+            const int n = g * kQG + (lane & 31);
+            const uint16_t* qp = a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + c0;
+            uint4 codes[4];
+            const float scale = quant_q_group(qp, n < a.N, codes);
+            int8_t* out = a.q_i8 + ((int64_t)bh * a.G + g) * kQGroupBytes + lane * 16;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) *(uint4*)(out + kk * 64 * 16) = codes[kk];
+            if (lane == 0) a.q_scale[(int64_t)bh * a.G + g] = scale;
+        }
+    } else if (kv) {
+        // this wave's share of the tile's absolute maximum of K - k_mean
+        const bool valid = kn < a.N;
+        const uint16_t* kp = a.k + b * a.k_sb + (int64_t)kn * a.k_sn + h * a.k_sh + c0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kraw[kk][0] = valid ? *(const uint4*)(kp + 32 * kk) : make_uint4(0, 0, 0, 0);
+            kraw[kk][1] = valid ? *(const uint4*)(kp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+        }
+        const float am = wave_max(valid ? k_row_amax(kraw, kmp) : 0.0f);
+        if (lane == 0) k_amax[half] = am;
+    }
+    if (kv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(uint4*)(&tile[vrow * kVRow + 32 * vseg + 8 * i]) = vraw[i];
+    }
+    __syncthreads();
+    if (!kv) return;
+
+    if (wave >= 2) {
+        const float scale = k_codes(kraw, kmp, fmaxf(k_amax[0], k_amax[1]), kn < a.N,
+                                    a.k_i8 + ((int64_t)bh * a.T + t) * kTileBytes, half, lane);
+        if (wave == 2 && lane == 0) {
+            a.k_scale[(int64_t)bh * a.T + t] = scale;
+            // the head's largest K scale: scales are >= 0, so their bit
+            // patterns order as the values do
+            atomicMax((unsigned int*)a.k_scale_max + bh, __float_as_uint(scale));
+        }
+    }
+    v_codes(tile, a.v_inv + (int64_t)bh * kHD, a.v_scale + (int64_t)bh * kHD,
+            a.v_fp8 + ((int64_t)bh * a.T + t) * kTileBytes);
+}
+
+// K and V quantization with the RMSNorm + RoPE producer applied to K (Q is
+// quantized by tile_stats_nr or by the mainloop): one block of 256 threads
+// per (tile t, heads bh0 and bh0 + 1), see pair_item.  Wave w loads K rows
+// 32*(w%2) + l%32 of head bh0 + w/2, normalises and rotates them, and takes
+// their share of the tile's absolute maximum of K - k_mean; every thread
+// stages 32 channels of one V row of each head in LDS.  After the barrier
+// each wave writes the codes of its 32 K rows and the block writes both V
+// tiles (v_codes).
+__global__ __launch_bounds__(256) void quant_kv_nr_kernel(QuantArgs a) {
+    __shared__ uint16_t tile[2][kBK * kVRow];
+    __shared__ float k_amax[2][2];
+    int t, bh0;
+    pair_item(a.BH, t, bh0);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int hs = wave >> 1, half = wave & 1;
+    const int bh = bh0 + hs;
+    const bool head = bh < a.BH;     // uniform per wave
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int c0 = 16 * (lane >> 5);
+    const int kn = t * kBK + 32 * half + (lane & 31);
+    const bool valid = head && kn < a.N;
+    uint4 w[8];
+    load_row_words(a.k + b * a.k_sb + (int64_t)kn * a.k_sn + h * a.k_sh + c0, valid, w);
+    {
+        const int vrow = threadIdx.x >> 2;
+        const int vseg = threadIdx.x & 3;
+        const int n = t * kBK + vrow;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int bv = bh0 + sl;
+            if (bv >= a.BH) break;
+            const int vb = bv / a.H, vh = bv - vb * a.H;
+            const uint16_t* vp = a.v + vb * a.v_sb + (int64_t)n * a.v_sn + vh * a.v_sh + 32 * vseg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(uint4*)(&tile[sl][vrow * kVRow + 32 * vseg + 8 * i]) =
+                    n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;
+    uint4 kraw[4][2];
+    if (head) {
+        const int na = valid ? kn : 0;
+        norm_rope_row(w, lane >> 5, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2),
+                      a.nr.sin + (int64_t)na * (kHD / 2), a.nr.eps);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) { kraw[kk][0] = w[2 * kk]; kraw[kk][1] = w[2 * kk + 1]; }
+        const float am = wave_max(valid ? k_row_amax(kraw, kmp) : 0.0f);
+        if (lane == 0) k_amax[hs][half] = am;
+    }
+    __syncthreads();
+    if (head) {
+        const float scale = k_codes(kraw, kmp, fmaxf(k_amax[hs][0], k_amax[hs][1]), kn < a.N,
+                                    a.k_i8 + ((int64_t)bh * a.T + t) * kTileBytes, half, lane);
+        if (half == 0 && lane == 0) {
+            a.k_scale[(int64_t)bh * a.T + t] = scale;
+            atomicMax((unsigned int*)a.k_scale_max + bh, __float_as_uint(scale));
+        }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+        const int bv = bh0 + sl;
+        if (bv >= a.BH) break;
+        v_codes(tile[sl], a.v_inv + (int64_t)bv * kHD, a.v_scale + (int64_t)bv * kHD,
+                a.v_fp8 + ((int64_t)bv * a.T + t) * kTileBytes);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
     const int64_t BH = (int64_t)p.B * p.H;
+    const int64_t pairs = (BH + 1) / 2;    // head pairs of the RMSNorm + RoPE kernels
     {
         StatsArgs a;
         a.k = p.k; a.k_sb = p.k_sb; a.k_sn = p.k_sn; a.k_sh = p.k_sh;
@@ -407,8 +484,11 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
         a.H = p.H; a.N = p.N; a.T = p.T; a.BH = (int)BH; a.units = BH * p.T;
         a.k_tile_sum = p.k_tile_sum; a.v_tile_amax = p.v_tile_amax;
         a.nr = p.nr;
+        a.q = p.with_q ? p.q : nullptr; a.q_sb = p.q_sb; a.q_sn = p.q_sn; a.q_sh = p.q_sh;
+        a.G = p.G; a.q_i8 = p.q_i8; a.q_scale = p.q_scale;
         if (p.norm_rope) {
-            hipLaunchKernelGGL(tile_stats_nr_kernel, dim3((unsigned)a.units), dim3(256), 0, stream, a);
+            const int64_t tiles = p.with_q ? p.G / 2 : p.T;
+            hipLaunchKernelGGL(tile_stats_nr_kernel, dim3((unsigned)(pairs * tiles)), dim3(256), 0, stream, a);
         } else {
             const int64_t threads = a.units * 16;
             hipLaunchKernelGGL(tile_stats_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
@@ -423,19 +503,19 @@ hipError_t launch_prepass(const PrepassArgs& p, hipStream_t stream) {
     }
     {
         QuantArgs a;
-        a.q = p.with_q ? p.q : nullptr; a.q_sb = p.q_sb; a.q_sn = p.q_sn; a.q_sh = p.q_sh;
+        a.q = p.with_q && !p.norm_rope ? p.q : nullptr; a.q_sb = p.q_sb; a.q_sn = p.q_sn; a.q_sh = p.q_sh;
         a.k = p.k; a.k_sb = p.k_sb; a.k_sn = p.k_sn; a.k_sh = p.k_sh;
         a.v = p.v; a.v_sb = p.v_sb; a.v_sn = p.v_sn; a.v_sh = p.v_sh;
         a.H = p.H; a.N = p.N; a.T = p.T; a.G = p.G; a.BH = (int)BH;
-        a.Tq = p.with_q ? p.G / 2 : p.T;
+        a.Tq = a.q != nullptr ? p.G / 2 : p.T;
         a.k_mean = p.k_mean; a.v_inv = p.v_inv; a.v_scale = p.v_scale;
         a.q_i8 = p.q_i8; a.q_scale = p.q_scale; a.k_i8 = p.k_i8; a.k_scale = p.k_scale; a.v_fp8 = p.v_fp8;
         a.k_scale_max = p.k_scale_max;
         a.nr = p.nr;
         if (p.norm_rope)
-            hipLaunchKernelGGL(quant_qkv_kernel<true>, dim3((unsigned)(BH * a.Tq)), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(quant_kv_nr_kernel, dim3((unsigned)(pairs * p.T)), dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL(quant_qkv_kernel<false>, dim3((unsigned)(BH * a.Tq)), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(quant_qkv_kernel, dim3((unsigned)(BH * a.Tq)), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }

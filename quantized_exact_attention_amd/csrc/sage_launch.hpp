@@ -24,6 +24,10 @@ struct StatsArgs {
     float* k_tile_sum;
     float* v_tile_amax;
     NormRopeArgs nr;
+    // RMSNorm + RoPE pass only: the Q groups it quantizes as well (q null: none)
+    const uint16_t* q; int64_t q_sb, q_sn, q_sh;
+    int G;
+    int8_t* q_i8; float* q_scale;
 };
 
 struct FinalizeArgs {

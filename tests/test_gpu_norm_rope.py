@@ -98,6 +98,16 @@ def test_norm_rope_batched_bit_exact(sage, layout):
     _check_bytes(_run(sage, inp, p), ref, w)
 
 
+@pytest.mark.parametrize("B", [2, 3])
+def test_norm_rope_head_pairs_bit_exact(sage, B):
+    """Three heads per batch: with B = 2 a block's two heads belong to
+    different batch entries; with B = 3 the head count B*H is odd and the
+    last block has one head."""
+    _log("norm_rope quant parity: B=%d H=3 N=150" % B)
+    w, inp, p, ref = _case("n=150", B=B)
+    _check_bytes(_run(sage, inp, p), ref, w)
+
+
 @pytest.mark.parametrize("n", [1, 2, 33])
 def test_norm_rope_short_sequences_bit_exact(sage, n):
     _log("norm_rope quant parity: N=%d" % n)
