@@ -324,6 +324,38 @@ def test_attention_parity_large_logits(sage, factor, sm_scale, form):
     assert max_abs <= MAX_ABS and cos >= MIN_COS and exact >= MIN_BIT_EQUAL
 
 
+@pytest.mark.parametrize("factor,sm_scale,form", [(1, None, "fused"), (96, 3.0, "stepwise")])
+def test_range_call_equals_full_call_both_forms(sage, factor, sm_scale, form):
+    """H = 3, N = 12000 (3 x 94 workgroups, more than one per CU on part of
+    the chip): a one-head range call (94 workgroups) writes the same bytes
+    as the full call, in either score form, and sampled rows of the full
+    call meet the bar against the oracle, bit-equality included."""
+    import oracle
+    w = workloads.Workload("range_x%d" % factor, 1, 12000, 3, seed=34)
+    inp = workloads.generate(w)
+    q = (inp.q.float() * factor).bfloat16()
+    k = (inp.k.float() * factor).bfloat16()
+    qz_ref = oracle.quantize(q, k, inp.v)
+    steps = _stepwise_groups(qz_ref, sm_scale if sm_scale is not None else 128 ** -0.5)
+    nonempty = qz_ref.q_scale > 0
+    assert np.all(steps[nonempty]) if form == "stepwise" else not np.any(steps)
+    qz = sage.quantize_qkv(q.cuda(), k.cuda(), inp.v.cuda())
+    full = sage.attn_fwd_quantized(qz, sm_scale=sm_scale)
+    part = sage.attn_fwd_quantized_range(qz, 0, w.N, 1, 1, sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(part.view(torch.int16), full[:, :, 1:2].view(torch.int16))
+    rng = np.random.default_rng(35)
+    rr = np.concatenate([np.arange(32), np.arange(w.N - 40, w.N), rng.integers(0, w.N, 60)])
+    rows = np.array([[0, h, int(r)] for h in range(3) for r in rr], np.int64)
+    rb, _ = oracle.attn_rows(qz_ref, rows, sm_scale)
+    gb = full.view(torch.int16).cpu().numpy().view(np.uint16)[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got, ref = _dec_bf16(gb).astype(np.float64), _dec_bf16(rb).astype(np.float64)
+    max_abs, cos, exact = float(np.max(np.abs(got - ref))), _cos(got, ref), float(np.mean(gb == rb))
+    _log("range vs full x%d (%s): full call vs oracle max_abs=%.3g cos=%.7f bit-equal=%.3f"
+         % (factor, form, max_abs, cos, exact))
+    assert max_abs <= MAX_ABS and cos >= MIN_COS and exact >= MIN_BIT_EQUAL
+
+
 # ----------------------------------------------------- structural behaviour --
 
 def test_deterministic_and_two_call_path_identical(sage):
