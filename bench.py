@@ -27,7 +27,9 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
               wave tile of the contract's per-score vector work (and of that
               work plus the tile's matrix instructions) at three waves per
               SIMD, times the tiles per SIMD, at the clock measured under that
-              load; frac = that floor with the matrix work / the mainloop time
+              load; frac = that floor with the matrix work / the mainloop time;
+              the same at the mainloop's own counter-measured clock
+              (frac_at_mainloop_clock) while the counter summary holds
   cpu_baseline the CPU oracle on the host cores: the prepass of the whole
               workload in full, whole query rows of one head over all keys
               extrapolated to every row and head, and the 4096-token,
@@ -91,10 +93,12 @@ def recorded_traffic(workload):
 
 def recorded_pipes(workload):
     """MFMA busy share of SIMD cycles, matrix ops per active cycle against the
-    dense peak (at the clock the chip actually ran), and VALU active share of
-    the mainloop, from the committed counter summary, or None."""
+    dense peak (at the clock the chip actually ran), VALU active share and the
+    average clock of the mainloop (active cycles over its time), from the
+    committed counter summary, or None."""
     return recorded_fields(COUNTERS_FILE, workload,
-                           ("mfma_busy_frac", "mfma_ops_per_active_cycle_frac", "valu_active_frac"))
+                           ("mfma_busy_frac", "mfma_ops_per_active_cycle_frac", "valu_active_frac",
+                            "mainloop_clock_ghz"))
 
 
 def log(msg):
@@ -116,7 +120,7 @@ def prepass_bytes(B, N, H):
     return reads + writes
 
 
-def vector_roofline(sage, dev, stream, w, mainloop_ms):
+def vector_roofline(sage, dev, stream, w, mainloop_ms, pipes=None):
     """The mainloop's vector floor, measured on this GPU: the shader clock
     cycles one SIMD spends on one 32-query x 64-key wave tile of the
     contract's per-score vector work alone, and with the tile's 12 matrix
@@ -142,10 +146,18 @@ def vector_roofline(sage, dev, stream, w, mainloop_ms):
     tiles = w.B * w.H * -(-w.N // 32) * -(-w.N // 64) / (4.0 * cus)
     floor_v = cycles[0] * tiles / clock * 1e3
     floor_vm = cycles[1] * tiles / clock * 1e3
-    return {"bound": "valu", "unit": "ms", "cycles_per_tile_vector": cycles[0],
-            "cycles_per_tile_vector_matrix": cycles[1], "clock_ghz": clock / 1e9, "tiles_per_simd": tiles,
-            "floor_ms": floor_v, "floor_with_matrix_ms": floor_vm, "achieved_ms": mainloop_ms,
-            "frac": floor_vm / mainloop_ms}
+    r = {"bound": "valu", "unit": "ms", "cycles_per_tile_vector": cycles[0],
+         "cycles_per_tile_vector_matrix": cycles[1], "clock_ghz": clock / 1e9, "tiles_per_simd": tiles,
+         "floor_ms": floor_v, "floor_with_matrix_ms": floor_vm, "achieved_ms": mainloop_ms,
+         "frac": floor_vm / mainloop_ms}
+    # The same floor at the clock the counters recorded under the mainloop
+    # itself (it runs slower than under the probe), while that record holds.
+    if pipes and pipes.get("mainloop_clock_ghz"):
+        f = pipes["mainloop_clock_ghz"] * 1e9
+        r["mainloop_clock_ghz_counters"] = f / 1e9
+        r["floor_with_matrix_ms_at_mainloop_clock"] = cycles[1] * tiles / f * 1e3
+        r["frac_at_mainloop_clock"] = cycles[1] * tiles / f * 1e3 / mainloop_ms
+    return r
 
 
 def cpu_model():
@@ -379,6 +391,7 @@ def main():
             torch.cuda.synchronize(dev)
             nr_one_ms = n_start.elapsed_time(n_end) / args.steps
             log("bench: norm+rope one-call step %.3f ms" % nr_one_ms)
+    pipes = recorded_pipes(w.name)
     result = {
         "metric": METRIC,
         "value": ops / (ms_per_step * 1e-3) / 1e12,
@@ -411,8 +424,8 @@ def main():
         "norm_rope_prepass_gbps": prepass_bytes(w.B, w.N, w.H) / (nr_ms * 1e-3) / 1e9 if nr_ms else None,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
-        "mainloop_pipes": recorded_pipes(w.name),
-        "roofline_vector": vector_roofline(sage, dev, stream, w, main_avg),
+        "mainloop_pipes": pipes,
+        "roofline_vector": vector_roofline(sage, dev, stream, w, main_avg, pipes),
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
