@@ -293,8 +293,10 @@ sage_status sage_debug_qk_s32(const sage_quantized* qz, int32_t* s_out, void* st
  * values; |x| must be below 464 for a finite code.  Errors: INVALID_ARGUMENT, HIP. */
 sage_status sage_debug_cvt_e4m3(const float* x, uint8_t* y, int64_t n, void* stream);
 
-/* Shader clock cycles of the mainloop's tile step on this GPU (the vector
- * roofline the benchmark reports next to the matrix one).  Launches `blocks`
+/* Measurement support, not an operation of the pages: shader clock cycles of
+ * the mainloop's tile step on this GPU (the vector roofline the benchmark
+ * reports next to the matrix one; the per-score work it issues is that of
+ * "Sage2 Blackwell Mainloop", Existing Contract, as the mainloop does it).  Launches `blocks`
  * workgroups of 4*waves_per_simd waves (waves_per_simd waves on each SIMD of a
  * CU); every wave runs `iters` repetitions of one instruction stream and
  * stores the cycles it took (s_memtime difference) at
