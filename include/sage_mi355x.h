@@ -35,13 +35,13 @@
  *   - Inputs must be finite BF16 values; non-finite inputs give unspecified
  *     (but memory-safe) results.  Outputs follow the step-by-step definition
  *     below up to the hardware exp2 and the order of FP32 sums, which can move
- *     a probability to the adjacent E4M3 code at a rounding midpoint.  A
- *     32-row query group whose scores are bounded by 2^12 in log2 units
- *     (score * sm_scale * log2(e); the bound is 127 * the largest L1 norm of
- *     the group's Q codes * q_scale * the head's largest k_scale * sm_scale *
- *     log2(e)) forms each probability as 2^(S*sj + log2(448) - m) with a single
- *     rounding; every other group takes the definition's three roundings one
- *     by one, for any finite input.  Where an intermediate of the definition
+ *     a probability to the adjacent E4M3 code at a rounding midpoint.  Where
+ *     each of the four 32-row query groups of a 128-row block has its scores
+ *     bounded by 2^12 in log2 units (score * sm_scale * log2(e); the bound is
+ *     127 * the largest L1 norm of the group's Q codes * q_scale * the head's
+ *     largest k_scale * sm_scale * log2(e)), the block forms each probability
+ *     as 2^(S*sj + log2(448) - m) with a single rounding; every other block
+ *     takes the definition's three roundings one by one, for any finite input.  Where an intermediate of the definition
  *     overflows FP32 (input magnitudes near the BF16 range), the outputs do
  *     too.
  */

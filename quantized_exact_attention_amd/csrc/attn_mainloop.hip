@@ -317,37 +317,84 @@ __device__ __forceinline__ void attend(const MainloopArgs& a, const WaveCtx& w, 
     int8_t* vc = w.lds_v;
     int8_t* vn = w.lds_v + kTileBytes;
     int8_t* vf = w.lds_v + 2 * kTileBytes;
-    for (int j = 0; j < T - 1; ++j) {
-        tile_to_lds(w.kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, w.voff, w.wave);
-        tile_to_lds(w.vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, w.voff, w.wave);
-        if (w.active) {
-            // softmax of tile j, the alpha rescale of RO (skipped when no row
-            // of the wave changed its max), PV of tile j, QK of tile j+1
+    if constexpr (kStepwise) {
+        for (int j = 0; j < T - 1; ++j) {
+            tile_to_lds(w.kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, w.voff, w.wave);
+            tile_to_lds(w.vg + (int64_t)min(j + 2, T - 1) * kTileBytes, vf, w.voff, w.wave);
+            if (w.active) {
+                // softmax of tile j, the alpha rescale of RO (skipped when no
+                // row of the wave changed its max), PV of tile j, QK of tile j+1
+                float alpha;
+                v8i pk;
+                bool moved;
+                softmax_tile<kStepwise, false>(s0, s1, (w.qs * w.ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved,
+                                               pk);
+                if (moved) rescale(ro, alpha);
+                SAGE_FENCE();
+                pv_tile(vc, pk, lane, ro);
+                qk_tile(kq, qf, lane, s0, s1, bias);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
+            block_barrier();
+            int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
+            t = vf;  vf = vc;  vc = vn;  vn = t;
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (!w.active) return;
+        {
+            const int j = T - 1;
             float alpha;
             v8i pk;
             bool moved;
-            softmax_tile<kStepwise, false>(s0, s1, (w.qs * w.ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
+            softmax_tile<kStepwise, true>(s0, s1, (w.qs * w.ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha,
+                                          moved, pk);
             if (moved) rescale(ro, alpha);
-            SAGE_FENCE();
-            pv_tile(vc, pk, lane, ro);
-            qk_tile(kq, qf, lane, s0, s1, bias);
+            pv_tile(vc, pk, lane, ro);                   // V(T-1)
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j+1) have landed
+    } else {
+        // Fused form: each tile's PV moves to the start of the next
+        // iteration, ahead of that tile's softmax, so that the matrix pipe
+        // works through the softmax's vector instructions.  RO still
+        // receives every tile's PV in tile order, each after its own tile's
+        // alpha rescale and before the next tile's.  V slots by role: vp
+        // holds V(j-1) for iteration j's PV, vc V(j), and vf receives V(j+1)
+        // (the V tile of iteration j+2's PV, as far ahead as before).
+        int8_t* vp = vn;
+        v8i pkprev;
+        for (int j = 0; j < T - 1; ++j) {
+            tile_to_lds(w.kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, w.voff, w.wave);
+            tile_to_lds(w.vg + (int64_t)(j + 1) * kTileBytes, vf, w.voff, w.wave);
+            if (w.active) {
+                float alpha;
+                v8i pk;
+                bool moved;
+                if (j > 0) pv_tile(vp, pkprev, lane, ro);   // tile j-1
+                softmax_tile<false, false>(s0, s1, (w.qs * w.ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
+                if (moved) rescale(ro, alpha);
+                SAGE_FENCE();
+                qk_tile(kq, qf, lane, s0, s1, bias);
+                pkprev = pk;
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j) have landed
+            block_barrier();
+            int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
+            t = vp;  vp = vc;  vc = vf;  vf = t;
+        }
+        // V(T-1), loaded in the last iteration, has landed for every wave
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         block_barrier();
-        int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
-        t = vf;  vf = vc;  vc = vn;  vn = t;
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    if (!w.active) return;
-    {
-        const int j = T - 1;
-        float alpha;
-        v8i pk;
-        bool moved;
-        softmax_tile<kStepwise, true>(s0, s1, (w.qs * w.ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha,
+        if (!w.active) return;
+        {
+            const int j = T - 1;
+            float alpha;
+            v8i pk;
+            bool moved;
+            if (T > 1) pv_tile(vp, pkprev, lane, ro);   // tile T-2
+            softmax_tile<false, true>(s0, s1, (w.qs * w.ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha,
                                       moved, pk);
-        if (moved) rescale(ro, alpha);
-        pv_tile(vc, pk, lane, ro);                   // V(T-1)
+            if (moved) rescale(ro, alpha);
+            pv_tile(vc, pk, lane, ro);                   // V(T-1)
+        }
     }
 
     const float dtot = halves_sum(dpart);
@@ -379,6 +426,7 @@ __device__ __forceinline__ void attend(const MainloopArgs& a, const WaveCtx& w, 
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(MainloopArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t lds_k[kKSlots * kTileBytes];
     __shared__ __attribute__((aligned(16))) int8_t lds_v[kVSlots * kTileBytes];
+    __shared__ int form_flags[kWaves];   // per wave: its group needs the stepwise form
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int bhl = item / a.n_qblk;              // (b, head within the range)
@@ -454,13 +502,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
                      kScoreBias, kScoreBias};
     asm volatile("" : "+v"(bias));
 
-    // The score step's form for this wave (wave-uniform).  Every code has
-    // |code| <= 127, so |S| <= 127 * ||q||_1 for each query row q of the
+    // The score step's form for this workgroup.  Every code has
+    // |code| <= 127, so |S| <= 127 * ||q||_1 for each query row q of a
     // group and every key, and |t| = |S| * sj <= 127 * max ||q||_1 * qs *
-    // max_t k_scale[t] * c over every tile of the head.  The fused form is
-    // taken when that bound is below kStepwiseFrom.  ||q||_1 comes from the
-    // codes in registers (v_sad_u8 on the codes shifted to offset binary),
-    // the head's largest K scale from the prepass.
+    // max_t k_scale[t] * c over every tile of the head.  A wave's group may
+    // take the fused form when that bound is below kStepwiseFrom; the
+    // workgroup takes it when all four may (the waves share the K/V rings,
+    // and the two forms load and wait for them on different schedules), else
+    // the stepwise form, which is the definition's own rounding.  ||q||_1
+    // comes from the codes in registers (v_sad_u8 on the codes shifted to
+    // offset binary), the head's largest K scale from the prepass.
     uint32_t l1 = 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -471,10 +522,13 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     for (int o = 16; o >= 1; o >>= 1) l1 = max(l1, (uint32_t)__shfl_xor((int)l1, o, 64));
     const float ksmax = ((const_f32_ptr)a.k_scale_max)[bh];
     const float bound = ((127.0f * (float)l1) * qs) * (ksmax * c);
-    const bool stepwise = __builtin_amdgcn_readfirstlane(!(bound < kStepwiseFrom)) != 0;
+    if (lane == 0) form_flags[wave] = !(bound < kStepwiseFrom);
 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    bool stepwise = false;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) stepwise = stepwise || form_flags[i] != 0;
     // Each form runs from here to the stored output in its own copy of the
     // code, which keeps the register allocation of the two loops apart.
     const WaveCtx w{kg, vg, ksc, lds_k, lds_v, voff, wave, lane, active, qs, g, b, hl, bh};

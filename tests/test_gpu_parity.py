@@ -274,12 +274,13 @@ def test_attention_parity_other_scales(sage, sm_scale):
 
 
 def _stepwise_groups(qz, sm_scale):
-    """The kernel's choice of score step per 32-row group, recomputed in
-    float64 from the oracle's codes and scales: the stepwise form (t = S*sj,
-    x = t - m, p = 448*2^x, the definition's roundings) when 127 * the
-    largest L1 norm of a query row's codes * q_scale * the head's largest K
-    scale * sm_scale * log2(e) -- a bound on every |score| in log2 units -- is
-    at least 2^12, else the fused form p = 2^fma(S, sj, log2(448) - m)."""
+    """Which 32-row groups need the stepwise score step (t = S*sj, x = t - m,
+    p = 448*2^x, the definition's roundings), recomputed in float64 from the
+    oracle's codes and scales: those where 127 * the largest L1 norm of a
+    query row's codes * q_scale * the head's largest K scale * sm_scale *
+    log2(e) -- a bound on every |score| in log2 units -- is at least 2^12.
+    The kernel takes the stepwise form for every 128-row block that holds
+    such a group, the fused form p = 2^fma(S, sj, log2(448) - m) elsewhere."""
     c = sm_scale * np.log2(np.e)
     q = qz.q_i8.astype(np.int64)
     B, H, Nq, _ = q.shape
@@ -300,8 +301,8 @@ def test_attention_parity_large_logits(sage, factor, sm_scale, form):
     those of real attention (up to about 1e7 nats).  Waves whose scores are
     bounded below 2^12 take the fused score step, the others the stepwise
     one; either way the output meets the full bar, bit-equality included.
-    Rows beyond N = 300 leave the last groups empty, so some workgroups mix
-    waves of both forms."""
+    Rows beyond N = 300 leave the last groups empty (bound 0), so some
+    blocks hold groups of both kinds."""
     import oracle
     w = workloads.Workload("logits_x%d" % factor, 1, 300, 2, seed=33)
     inp = workloads.generate(w)
