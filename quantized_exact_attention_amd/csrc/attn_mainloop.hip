@@ -23,9 +23,12 @@
 //   * PV is O^T = V^T . P^T with the unscaled v_mfma_f32_32x32x64_f8f6f4,
 //     accumulating straight into the FP32 RO rows after the alpha rescale,
 //     tile by tile in increasing order.
-//   * Per iteration a wave runs a vector phase (the softmax of one tile) and
-//     then a matrix phase (that tile's PV and the next tile's QK); the three
-//     waves of a SIMD overlap each other's phases.
+//   * Per iteration a wave issues the previous tile's PV (four matrix
+//     instructions), runs the vector phase (the softmax of one tile) and
+//     then the next tile's QK; the PV runs under the wave's own softmax, and
+//     the three waves of a SIMD overlap each other's phases.  (Workgroups
+//     that take the stepwise score form keep each tile's PV after its own
+//     softmax.)
 //   * K and V tiles (8 KiB each, already in operand order) stream through
 //     three-slot LDS rings (48 KiB per workgroup) filled by direct
 //     global-to-LDS loads issued two tiles ahead of their use.
@@ -211,12 +214,13 @@ __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
 // LDS rings: K and V tiles in 3 slots each, filled straight from global
 // memory by global_load_lds_dwordx4 (no VGPR staging).  In iteration j a
 // wave runs the softmax of tile j (scores computed in the previous
-// iteration), the PV of tile j and the QK of tile j+1, while the workgroup's
-// loads of K(j+3) and V(j+2) are in flight; the loads issued one iteration
-// earlier are waited for before the barrier that ends the iteration.  The
-// slots change roles by pointer rotation, not by index arithmetic.  RO
-// receives every tile's PV in increasing tile order, each after the rescale
-// by that tile's alpha.
+// iteration), the PV of tile j-1 (fused score form; tile j in the stepwise
+// form) and the QK of tile j+1, while the workgroup's loads of K(j+3) and of
+// V(j+1) (V(j+2) in the stepwise form) are in flight; the loads issued one
+// iteration earlier are waited for before the barrier that ends the
+// iteration.  The slots change roles by pointer rotation, not by index
+// arithmetic.  RO receives every tile's PV in increasing tile order, each
+// after the rescale by that tile's alpha.
 constexpr int kKSlots = 3;
 constexpr int kVSlots = 3;
 
