@@ -115,15 +115,16 @@ __device__ __forceinline__ void pv_tile(const int8_t* vtile, const v8i& pk, int 
 // `tail` in the final, partial tile.  `moved` reports that some row maximum
 // of the wave moved, which is also exactly when RO needs the alpha rescale.
 //
-// Two forms of the score step (kStepwise), one per wave for the whole loop:
+// Two forms of the score step (kStepwise), one per workgroup for the whole
+// loop:
 //   * stepwise, the definition's roundings one by one: t = fl(S * sj),
 //     x = fl(t - m), p = fl(448 * 2^x);
 //   * fused, two vector instructions fewer per score: p = 2^fma(S, sj, off)
 //     with off = log2(448) - m, kept across tiles and recomputed when a row
 //     maximum moves.  It rounds once where the stepwise form rounds three
 //     times; the two differ by about one unit in the last place of m,
-//     relative, in p.  The fused form is taken only by waves whose scores are
-//     all bounded by 2^12 in magnitude (in log2 units, see
+//     relative, in p.  The fused form is taken only by workgroups whose
+//     scores are all bounded by 2^12 in magnitude (in log2 units, see
 //     kStepwiseFrom), where that difference is below 2^-11 of p, a small
 //     fraction of an E4M3 step; real attention has |m| of a few units.
 template <bool kStepwise, bool kLast>
@@ -200,8 +201,8 @@ __device__ __forceinline__ void softmax_tile(v16i& s0, v16i& s1, float sj, int t
 }
 
 // Scores of magnitude at or above this (log2 units) take the stepwise form.
-// A wave takes the fused form only when a bound on all of its scores lies
-// below it (see the kernel's prologue).
+// A workgroup takes the fused form only when a bound on all of its waves'
+// scores lies below it (see the kernel's prologue).
 constexpr float kStepwiseFrom = 4096.0f;   // 2^12
 
 __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
