@@ -208,8 +208,8 @@ __global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
     const int d = threadIdx.x;
     const float* ks = a.k_tile_sum + (int64_t)bh * a.T * kHD + d;
     const float* va = a.v_tile_amax + (int64_t)bh * a.T * kHD + d;
-    // Sequential in tile order; loads are issued 32 tiles ahead of the adds.
-    constexpr int kBatch = 32;
+    // Sequential in tile order; loads are issued 64 tiles ahead of the adds.
+    constexpr int kBatch = 64;
     float total = 0.0f, amax = 0.0f;
     int t = 0;
     for (; t + kBatch <= a.T; t += kBatch) {
