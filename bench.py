@@ -30,6 +30,10 @@ HBM before timing starts.  Prints ONE JSON line on stdout.
               load; frac = that floor with the matrix work / the mainloop time;
               the same at the mainloop's own counter-measured clock
               (frac_at_mainloop_clock) while the counter summary holds
+  matrix_achievable  the matrix pipes' measured rate for the mainloop's
+              instruction mix (8 INT8 and 4 FP8 matrix instructions per wave
+              tile, back to back on every CU, no other work), and the
+              mainloop's effective rate as a fraction of it
   cpu_baseline the CPU oracle on the host cores: the prepass of the whole
               workload in full, whole query rows of one head over all keys
               extrapolated to every row and head, and the 4096-token,
@@ -158,6 +162,38 @@ def vector_roofline(sage, dev, stream, w, mainloop_ms, pipes=None):
         r["floor_with_matrix_ms_at_mainloop_clock"] = cycles[1] * tiles / f * 1e3
         r["frac_at_mainloop_clock"] = cycles[1] * tiles / f * 1e3 / mainloop_ms
     return r
+
+
+# Matrix operations per wave per iteration of the issue probe's matrix stream:
+# one wave tile's 8 v_mfma_i32_32x32x32_i8 and 4 v_mfma_f32_32x32x64_f8f6f4,
+# 2 ops per multiply-add.
+PROBE_MATRIX_OPS_PER_ITER = 8 * 2 * 32 * 32 * 32 + 4 * 2 * 32 * 32 * 64
+
+
+def matrix_achievable(sage, dev, stream, achieved_tops):
+    """The matrix pipes' achievable rate on this GPU for the mainloop's own
+    instruction mix: the issue probe's matrix stream (the 12 independent-ish
+    matrix instructions of a wave tile, nothing else) on every CU, two waves
+    per SIMD, timed with HIP events; the better of two runs (the first may
+    include the clock's ramp).  frac = the mainloop's effective rate over it."""
+    import torch
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wps, blocks, iters = 2, 4 * cus, 2000
+    best = None
+    for _ in range(2):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sage.debug_issue_probe(2, wps, blocks, iters, dev)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    ops = blocks * 4 * wps * iters * PROBE_MATRIX_OPS_PER_ITER
+    tops = ops / (best * 1e-3) / 1e12
+    return {"tops": tops, "unit": "TOPS", "frac": achieved_tops / tops, "peak_frac": tops / PEAK_TOPS,
+            "sample": "%d workgroups of %d waves, %d iterations of 8 INT8 32x32x32 + 4 FP8 32x32x64 "
+                      "matrix instructions per wave" % (blocks, 4 * wps, iters)}
 
 
 def cpu_model():
@@ -426,6 +462,7 @@ def main():
                      "frac": achieved / PEAK_TOPS, "traffic": recorded_traffic(w.name)},
         "mainloop_pipes": pipes,
         "roofline_vector": vector_roofline(sage, dev, stream, w, main_avg, pipes),
+        "matrix_achievable": matrix_achievable(sage, dev, stream, achieved),
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

@@ -79,3 +79,11 @@ def test_more_than_one_gpu_is_refused(n):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_probe_matrix_ops_per_iteration():
+    # one wave tile's matrix work: 32 queries x 64 keys x 128 channels for QK
+    # and 32 queries x 128 channels x 64 keys for PV, 2 ops per multiply-add
+    assert bench.PROBE_MATRIX_OPS_PER_ITER == 2 * (32 * 64 * 128) + 2 * (32 * 128 * 64)
+    # a 64-query x 64-key block of the workload count holds two wave tiles
+    assert bench.PROBE_MATRIX_OPS_PER_ITER == bench.effective_ops(1, 64, 1) / 2
