@@ -85,23 +85,33 @@ __device__ __forceinline__ void pair_item(int BH, int& t, int& bh0) {
 
 // One row of 128 BF16 channels of the lane's share in the QK operand split
 // (lane l: row l%32, channels 32kk + 16*(l/32) + 0..15 in w[2kk], w[2kk+1]);
-// rows that are not valid read as zeros.
+// rows that are not valid read as zeros.  `p` points at a readable row in
+// every lane (callers substitute a row that exists for one that does not),
+// so the eight loads are issued together, outside any branch; the lanes
+// whose row is not valid then clear their words.
 __device__ __forceinline__ void load_row_words(const uint16_t* p, bool valid, uint4 (&w)[8]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        w[2 * kk] = valid ? *(const uint4*)(p + 32 * kk) : make_uint4(0, 0, 0, 0);
-        w[2 * kk + 1] = valid ? *(const uint4*)(p + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
+        w[2 * kk] = *(const uint4*)(p + 32 * kk);
+        w[2 * kk + 1] = *(const uint4*)(p + 32 * kk + 8);
+    }
+    if (!valid) {
+        // a real branch (taken only in a tile's last rows), not 32 selects
+        asm volatile("");
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = make_uint4(0, 0, 0, 0);
     }
 }
 
 // tile_stats with the RMSNorm + RoPE producer.  Wave w serves head bh0 + w/2
 // and rows 32*(w%2) .. +31 of tile t:
-//   * it loads those K rows, normalises and rotates them (norm_rope_row) and
-//     stages the BF16 results in LDS;
-//   * lane (c8 = l%16, rp = l/16) takes the absolute maxima of V channels
-//     8c8 .. 8c8+7 over its rows rp, rp+4, ..., rp+28 of the wave's 32; the
-//     four lanes of one c8 combine across the wave and leave the wave's 128
-//     channel maxima in LDS;
+//   * it loads those K rows and, with those loads still in flight, the V
+//     rows: lane (c8 = l%16, rp = l/16) takes the absolute maxima of V
+//     channels 8c8 .. 8c8+7 over its rows rp, rp+4, ..., rp+28 of the wave's
+//     32; the four lanes of one c8 combine across the wave and leave the
+//     wave's 128 channel maxima in LDS;
+//   * it normalises and rotates the K rows (norm_rope_row) and stages the
+//     BF16 results in LDS;
 //   * when Q is quantized in this pass, it does the same normalisation for
 //     Q group 2t + w%2 of its head and writes that group's INT8 codes and
 //     scale (blocks past the last K/V tile, t >= T, do only this: the Q
@@ -128,30 +138,27 @@ __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
         const int n = n0 + row;
         const bool valid = row < rows;
         uint4 w[8];
-        load_row_words(a.k + b * a.k_sb + (int64_t)n * a.k_sn + h * a.k_sh + 16 * hf, valid, w);
-        const int na = valid ? n : 0;
-        norm_rope_row(w, hf, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
-                      a.nr.eps);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                *(uint4*)(&tile[hs][row * kVRow + 32 * kk + 16 * hf + 8 * e]) = w[2 * kk + e];
+        load_row_words(a.k + b * a.k_sb + (int64_t)(valid ? n : n0) * a.k_sn + h * a.k_sh + 16 * hf, valid, w);
 
+        // V maxima first, with all eight row loads in flight together
+        // alongside the K row's: a row past the tile's end reads the tile's
+        // last row instead, which leaves the tile's maximum unchanged (the
+        // two halves' maxima are only used combined).
         const int c8 = lane & 15, rp = lane >> 4;
         const uint16_t* vp = a.v + b * a.v_sb + h * a.v_sh + 8 * c8;
+        uint4 vraw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            vraw[i] = *(const uint4*)(vp + (int64_t)(n0 + min(32 * half + rp + 4 * i, rows - 1)) * a.v_sn);
         float am[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) am[c] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = 32 * half + rp + 4 * i;
-            if (r < rows) {
-                float vf[8];
-                unpack8(*(const uint4*)(vp + (int64_t)(n0 + r) * a.v_sn), vf);
+            float vf[8];
+            unpack8(vraw[i], vf);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) am[c] = fmaxf(am[c], fabsf(vf[c]));
-            }
+            for (int c = 0; c < 8; ++c) am[c] = fmaxf(am[c], fabsf(vf[c]));
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -162,13 +169,22 @@ __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) vam[hs][half][8 * c8 + c] = am[c];
         }
+
+        const int na = valid ? n : 0;
+        norm_rope_row(w, hf, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
+                      a.nr.eps);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                *(uint4*)(&tile[hs][row * kVRow + 32 * kk + 16 * hf + 8 * e]) = w[2 * kk + e];
     }
     if (a.q != nullptr && head) {
         const int g = 2 * t + half;
         const int n = g * kQG + (lane & 31);
         const bool valid = n < a.N;
         uint4 w[8];
-        load_row_words(a.q + b * a.q_sb + (int64_t)n * a.q_sn + h * a.q_sh + 16 * hf, valid, w);
+        load_row_words(a.q + b * a.q_sb + (int64_t)min(n, a.N - 1) * a.q_sn + h * a.q_sh + 16 * hf, valid, w);
         const int na = valid ? n : 0;
         norm_rope_row(w, hf, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
                       a.nr.eps);
@@ -426,21 +442,36 @@ __global__ __launch_bounds__(256) void quant_kv_nr_kernel(QuantArgs a) {
     const int kn = t * kBK + 32 * half + (lane & 31);
     const bool valid = head && kn < a.N;
     uint4 w[8];
-    load_row_words(a.k + b * a.k_sb + (int64_t)kn * a.k_sn + h * a.k_sh + c0, valid, w);
+    {
+        // waves of a missing second head read the first head's row
+        const int bl = head ? bh : bh0;
+        const int bb = bl / a.H, hh = bl - bb * a.H;
+        load_row_words(a.k + bb * a.k_sb + (int64_t)min(kn, a.N - 1) * a.k_sn + hh * a.k_sh + c0, valid, w);
+    }
     {
         const int vrow = threadIdx.x >> 2;
         const int vseg = threadIdx.x & 3;
         const int n = t * kBK + vrow;
+        // all eight loads in flight together: rows past the end read row
+        // N - 1 and stage zeros; the second head of a pair past the last
+        // head reads the first head's row and stages nothing
+        const int nl = min(n, a.N - 1);
+        uint4 vraw[2][4];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
-            const int bv = bh0 + sl;
-            if (bv >= a.BH) break;
+            const int bv = min(bh0 + sl, a.BH - 1);
             const int vb = bv / a.H, vh = bv - vb * a.H;
-            const uint16_t* vp = a.v + vb * a.v_sb + (int64_t)n * a.v_sn + vh * a.v_sh + 32 * vseg;
+            const uint16_t* vp = a.v + vb * a.v_sb + (int64_t)nl * a.v_sn + vh * a.v_sh + 32 * vseg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vraw[sl][i] = *(const uint4*)(vp + 8 * i);
+        }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            if (bh0 + sl >= a.BH) break;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *(uint4*)(&tile[sl][vrow * kVRow + 32 * vseg + 8 * i]) =
-                    n < a.N ? *(const uint4*)(vp + 8 * i) : make_uint4(0, 0, 0, 0);
+                    n < a.N ? vraw[sl][i] : make_uint4(0, 0, 0, 0);
         }
     }
     const float* kmp = a.k_mean + (int64_t)bh * kHD + c0;

@@ -168,8 +168,9 @@ __device__ __forceinline__ uint32_t& word_of(uint4& w, int m) {
 // each result rounded to BF16, in place on the row's BF16 words.  The row is
 // held by lanes l%32 and l%32 + 32 of a wave in the QK operand split: on the
 // lane with hf = l/32, w[2kk + e] holds channels 32kk + 16hf + 8e + 0..7.
-//   ss  = sum over channels 0..127 in order of fl(x*x), from +0 (both lanes
-//         see both halves through v_permlane32_swap and sum identically)
+//   ss  = sum over channels 0..127 in order of fl(x*x), from +0 (the running
+//         sum passes between the row's two lanes segment by segment, and both
+//         end with the same value)
 //   r   = fl(1 / fl(sqrt(fl(fl(ss / 128) + eps))))
 //   y_c = bf16(fl(fl(x_c * r) * g[c]))
 //   o_i = bf16(fl(fl(y_i * cos_i) - fl(y_{i+64} * sin_i))),
@@ -178,32 +179,32 @@ __device__ __forceinline__ uint32_t& word_of(uint4& w, int m) {
 // Channel i and i + 64 sit on the same lane (kk and kk + 2).
 __device__ __forceinline__ void norm_rope_row(uint4 (&w)[8], int hf, const float* g, const float* cos_row,
                                               const float* sin_row, float eps) {
+    // ss in channel order: 16-channel segment s = c/16 is block kk = s/2 of
+    // the lanes with hf = s%2.  Each lane squares its own 64 channels once;
+    // the running sum then alternates between the row's two lanes: at
+    // segment s every lane adds its block s/2 onto the running sum (the
+    // result is the sum's next value on the lanes that hold segment s), and
+    // v_permlane32_swap gives that value to both lanes for the next segment.
     float ss = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        uint32_t h0[8], h1[8];
+        float sq[16];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const uint32_t u = word_of(w[2 * kk + m / 4], m % 4);
-            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-            h0[m] = r[0];
-            h1[m] = r[1];
-        }
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float a = __uint_as_float(h0[m] << 16), b = __uint_as_float(h0[m] & 0xffff0000u);
-            const float a2 = a * a;
-            ss = ss + a2;
-            const float b2 = b * b;
-            ss = ss + b2;
-        }
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t u = word_of(w[2 * kk + e], m);
+                const float a = __uint_as_float(u << 16), b = __uint_as_float(u & 0xffff0000u);
+                sq[8 * e + 2 * m] = a * a;
+                sq[8 * e + 2 * m + 1] = b * b;
+            }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float a = __uint_as_float(h1[m] << 16), b = __uint_as_float(h1[m] & 0xffff0000u);
-            const float a2 = a * a;
-            ss = ss + a2;
-            const float b2 = b * b;
-            ss = ss + b2;
+        for (int owner = 0; owner < 2; ++owner) {
+            float t = ss;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t = t + sq[i];
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            ss = __uint_as_float(r[owner]);
         }
     }
     const float ms = ss / 128.0f;
