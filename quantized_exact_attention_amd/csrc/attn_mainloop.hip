@@ -219,9 +219,10 @@ __device__ __forceinline__ void rescale(v16f (&ro)[4], float alpha) {
 // form) and the QK of tile j+1, while the workgroup's loads of K(j+3) and of
 // V(j+1) (V(j+2) in the stepwise form) are in flight; the loads issued one
 // iteration earlier are waited for before the barrier that ends the
-// iteration.  The slots change roles by pointer rotation, not by index
-// arithmetic.  RO receives every tile's PV in increasing tile order, each
-// after the rescale by that tile's alpha.
+// iteration.  The fused form runs three iterations per loop pass, so that
+// every slot is a constant LDS offset (fused_step); the stepwise form
+// rotates slot pointers.  RO receives every tile's PV in increasing tile
+// order, each after the rescale by that tile's alpha.
 constexpr int kKSlots = 3;
 constexpr int kVSlots = 3;
 
@@ -240,7 +241,8 @@ __device__ __forceinline__ void tile_to_lds(const int8_t* gtile, int8_t* slot, u
 #pragma unroll
     for (int i = 0; i < kTileLoads; ++i) {
         const int part = wave * kTileLoads + i;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(slot + part * 1024));
+        // wave-uniform (wave is), so the compiler forms it in an SGPR
+        const uint32_t dst = (uint32_t)(uintptr_t)(slot + part * 1024);
         uint32_t saved_m0;
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
@@ -288,6 +290,43 @@ struct WaveCtx {
     float qs;              // the group's Q scale
     int g, b, hl, bh;      // group, batch entry, head within the range, b*H + h
 };
+
+// Fused score form: LDS slot of K tile i is i % 3; V tile i sits in slot
+// (3 - i % 3) % 3 (tile 0 in slot 0 from the prologue, then each iteration j
+// loads V(j+1) into the slot that V(j-2) has left).
+__device__ __forceinline__ int fused_v_slot(int i) { return (3 - i % 3) % 3; }
+
+// Iteration j of the fused-form tile loop, j % 3 == kPhase: the loads of
+// K(j+3) and V(j+1), the PV of tile j-1, the softmax of tile j with the alpha
+// rescale of RO, the QK of tile j+1, then the wait for this iteration's loads
+// and the workgroup barrier.  The phase fixes every ring slot at compile
+// time, so the LDS reads address their slots through the instruction's
+// offset field (no per-iteration address arithmetic).
+template <int kPhase>
+__device__ __forceinline__ void fused_step(const MainloopArgs& a, const WaveCtx& w, const v4i (&qf)[4],
+                                           const v16i& bias, int j, v16i& s0, v16i& s1, float& m, float& off,
+                                           float& dpart, v16f (&ro)[4], v8i& pkprev) {
+    constexpr int kKFill = kPhase;                          // receives K(j+3)
+    constexpr int kKRead = (kPhase + 1) % 3;                // holds K(j+1)
+    constexpr int kVFill = (3 - (kPhase + 1) % 3) % 3;      // receives V(j+1)
+    constexpr int kVRead = (3 - (kPhase + 2) % 3) % 3;      // holds V(j-1)
+    tile_to_lds(w.kg + (int64_t)min(j + 3, a.T - 1) * kTileBytes, w.lds_k + kKFill * kTileBytes, w.voff, w.wave);
+    tile_to_lds(w.vg + (int64_t)(j + 1) * kTileBytes, w.lds_v + kVFill * kTileBytes, w.voff, w.wave);
+    if (w.active) {
+        float alpha;
+        v8i pk;
+        bool moved;
+        if (j > 0) pv_tile(w.lds_v + kVRead * kTileBytes, pkprev, w.lane, ro);   // tile j-1
+        softmax_tile<false, false>(s0, s1, (w.qs * w.ksc[j]) * a.c, 0, w.lane, m, off, dpart, alpha, moved, pk);
+        if (moved) rescale(ro, alpha);
+        SAGE_FENCE();
+        qk_tile(w.lds_k + kKRead * kTileBytes, qf, w.lane, s0, s1, bias);
+        pkprev = pk;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j) have landed
+    block_barrier();
+    SAGE_FENCE();
+}
 
 // One wave from the QK of tile 0 to its stored output rows, in one form of
 // the score step: the tile loop, the last (partial) tile, then 1/d, the V
@@ -361,44 +400,33 @@ __device__ __forceinline__ void attend(const MainloopArgs& a, const WaveCtx& w, 
         // iteration, ahead of that tile's softmax, so that the matrix pipe
         // works through the softmax's vector instructions.  RO still
         // receives every tile's PV in tile order, each after its own tile's
-        // alpha rescale and before the next tile's.  V slots by role: vp
-        // holds V(j-1) for iteration j's PV, vc V(j), and vf receives V(j+1)
-        // (the V tile of iteration j+2's PV, as far ahead as before).
-        int8_t* vp = vn;
+        // alpha rescale and before the next tile's.  Iteration j loads
+        // V(j+1), the V tile of iteration j+2's PV (as far ahead as the
+        // stepwise form).  The loop runs three iterations (the rings'
+        // period) per pass, so that each has its slots fixed (fused_step).
         v8i pkprev;
-        for (int j = 0; j < T - 1; ++j) {
-            tile_to_lds(w.kg + (int64_t)min(j + 3, T - 1) * kTileBytes, kf, w.voff, w.wave);
-            tile_to_lds(w.vg + (int64_t)(j + 1) * kTileBytes, vf, w.voff, w.wave);
-            if (w.active) {
-                float alpha;
-                v8i pk;
-                bool moved;
-                if (j > 0) pv_tile(vp, pkprev, lane, ro);   // tile j-1
-                softmax_tile<false, false>(s0, s1, (w.qs * w.ksc[j]) * c, 0, lane, m, off, dpart, alpha, moved, pk);
-                if (moved) rescale(ro, alpha);
-                SAGE_FENCE();
-                qk_tile(kq, qf, lane, s0, s1, bias);
-                pkprev = pk;
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitVmIter);   // K(j+2), V(j) have landed
-            block_barrier();
-            int8_t* t = kf;  kf = kq;  kq = kn;  kn = t;
-            t = vp;  vp = vc;  vc = vf;  vf = t;
+        int j = 0;
+        for (; j + 3 <= T - 1; j += 3) {
+            fused_step<0>(a, w, qf, bias, j, s0, s1, m, off, dpart, ro, pkprev);
+            fused_step<1>(a, w, qf, bias, j + 1, s0, s1, m, off, dpart, ro, pkprev);
+            fused_step<2>(a, w, qf, bias, j + 2, s0, s1, m, off, dpart, ro, pkprev);
         }
+        if (j < T - 1) fused_step<0>(a, w, qf, bias, j++, s0, s1, m, off, dpart, ro, pkprev);
+        if (j < T - 1) fused_step<1>(a, w, qf, bias, j++, s0, s1, m, off, dpart, ro, pkprev);
         // V(T-1), loaded in the last iteration, has landed for every wave
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         block_barrier();
         if (!w.active) return;
         {
-            const int j = T - 1;
+            const int jl = T - 1;
             float alpha;
             v8i pk;
             bool moved;
-            if (T > 1) pv_tile(vp, pkprev, lane, ro);   // tile T-2
-            softmax_tile<false, true>(s0, s1, (w.qs * w.ksc[j]) * c, a.N - j * kBK, lane, m, off, dpart, alpha,
+            if (T > 1) pv_tile(w.lds_v + fused_v_slot(T - 2) * kTileBytes, pkprev, lane, ro);   // tile T-2
+            softmax_tile<false, true>(s0, s1, (w.qs * w.ksc[jl]) * c, a.N - jl * kBK, lane, m, off, dpart, alpha,
                                       moved, pk);
             if (moved) rescale(ro, alpha);
-            pv_tile(vc, pk, lane, ro);                   // V(T-1)
+            pv_tile(w.lds_v + fused_v_slot(T - 1) * kTileBytes, pk, lane, ro);   // V(T-1)
         }
     }
 
@@ -440,7 +468,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
     const int h = a.h_start + hl;
     const int bh = b * a.H + h;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int lane = threadIdx.x & 63;
+    // the lane index from v_mbcnt (no inputs), which the compiler can recompute
+    // where it is needed instead of holding the work-item id for the whole loop
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     // this lane's byte offset in a tile for its first 1 KiB tile load
     const uint32_t voff = (uint32_t)((wave * kTileLoads * 64 + lane) * 16);
     const int g = a.g_begin + qb * kWaves + wave;
@@ -480,7 +510,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void mainloop_kernel(Mainl
                 w[2 * kk + 1] = valid ? *(const uint4*)(qp + 32 * kk + 8) : make_uint4(0, 0, 0, 0);
             }
             const int na = valid ? nq : 0;
-            norm_rope_row(w, lane >> 5, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2),
+            norm_rope_row<true>(w, lane >> 5, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2),
                           a.nr.sin + (int64_t)na * (kHD / 2), a.nr.eps);
             qs = quant_q_words(w, codes);
         } else {

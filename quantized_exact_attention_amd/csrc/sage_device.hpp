@@ -176,7 +176,11 @@ __device__ __forceinline__ uint32_t& word_of(uint4& w, int m) {
 //   o_i = bf16(fl(fl(y_i * cos_i) - fl(y_{i+64} * sin_i))),
 //   o_{i+64} = bf16(fl(fl(y_{i+64} * cos_i) + fl(y_i * sin_i))), i < 64,
 // with the angle row (cos_row, sin_row: 64 FP32 each) of the row's token.
-// Channel i and i + 64 sit on the same lane (kk and kk + 2).
+// Channel i and i + 64 sit on the same lane (kk and kk + 2).  kLowRegs: the
+// channel values are unpacked again for the normalisation rather than kept
+// from the squares (an empty asm per word hides that they are the same), for
+// callers that are short of registers; the results are identical.
+template <bool kLowRegs = false>
 __device__ __forceinline__ void norm_rope_row(uint4 (&w)[8], int hf, const float* g, const float* cos_row,
                                               const float* sin_row, float eps) {
     // ss in channel order: 16-channel segment s = c/16 is block kk = s/2 of
@@ -206,6 +210,11 @@ __device__ __forceinline__ void norm_rope_row(uint4 (&w)[8], int hf, const float
             const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
             ss = __uint_as_float(r[owner]);
         }
+    }
+    if (kLowRegs) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
     }
     const float ms = ss / 128.0f;
     const float t = ms + eps;
