@@ -121,6 +121,11 @@ __device__ __forceinline__ void load_row_words(const uint16_t* p, bool valid, ui
 __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
     __shared__ uint16_t tile[2][kBK * kVRow];
     __shared__ float vam[2][2][kHD];
+    // the RMSNorm weights of K and Q, read from LDS by every row: 64 fewer
+    // global loads per lane and row
+    __shared__ float wts[2][kHD];
+    wts[threadIdx.x >> 7][threadIdx.x & 127] = (threadIdx.x < 128 ? a.nr.k_weight : a.nr.q_weight)[threadIdx.x & 127];
+    __syncthreads();
     int t, bh0;
     pair_item(a.BH, t, bh0);
     const int wave = threadIdx.x >> 6;
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
         }
 
         const int na = valid ? n : 0;
-        norm_rope_row(w, hf, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
+        norm_rope_row(w, hf, wts[0], a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
                       a.nr.eps);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(256) void tile_stats_nr_kernel(StatsArgs a) {
         uint4 w[8];
         load_row_words(a.q + b * a.q_sb + (int64_t)min(n, a.N - 1) * a.q_sn + h * a.q_sh + 16 * hf, valid, w);
         const int na = valid ? n : 0;
-        norm_rope_row(w, hf, a.nr.q_weight, a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
+        norm_rope_row(w, hf, wts[1], a.nr.cos + (int64_t)na * (kHD / 2), a.nr.sin + (int64_t)na * (kHD / 2),
                       a.nr.eps);
         uint4 codes[4];
         const float scale = quant_q_words(w, codes);
@@ -430,6 +435,9 @@ __global__ __launch_bounds__(256) void quant_qkv_kernel(QuantArgs a) {
 __global__ __launch_bounds__(256) void quant_kv_nr_kernel(QuantArgs a) {
     __shared__ uint16_t tile[2][kBK * kVRow];
     __shared__ float k_amax[2][2];
+    __shared__ float wts[kHD];         // the RMSNorm weights of K, read from LDS by every row
+    if (threadIdx.x < kHD) wts[threadIdx.x] = a.nr.k_weight[threadIdx.x];
+    __syncthreads();
     int t, bh0;
     pair_item(a.BH, t, bh0);
     const int wave = threadIdx.x >> 6;
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(256) void quant_kv_nr_kernel(QuantArgs a) {
     uint4 kraw[4][2];
     if (head) {
         const int na = valid ? kn : 0;
-        norm_rope_row(w, lane >> 5, a.nr.k_weight, a.nr.cos + (int64_t)na * (kHD / 2),
+        norm_rope_row(w, lane >> 5, wts, a.nr.cos + (int64_t)na * (kHD / 2),
                       a.nr.sin + (int64_t)na * (kHD / 2), a.nr.eps);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) { kraw[kk][0] = w[2 * kk]; kraw[kk][1] = w[2 * kk + 1]; }
