@@ -440,6 +440,38 @@ def test_degenerate_short_sequences(sage, n):
     assert _cos(got, ref) >= MIN_COS
 
 
+@pytest.mark.parametrize("layout", ["separate", "projection"])
+def test_many_heads_short_sequence(sage, layout):
+    """B = 2, H = 2,500, N = 33: 5,000 heads of one partial tile each (5,000
+    workgroups with one active wave, the other three idle), through both
+    paths, every row against the oracle and every byte bit-exact."""
+    import oracle
+    w = workloads.Workload("heads_" + layout, 2, 33, 2500, seed=960, layout=layout)
+    _log("many heads: %s" % w.name)
+    inp = workloads.generate(w)
+    q, k, v = _to_gpu(inp)
+    qz = sage.quantize_qkv(q, k, v)
+    two = sage.attn_fwd_quantized(qz)
+    one = sage.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    ref, ref_bits, _ = oracle.attention(inp.q, inp.k, inp.v)
+    B, N, H = w.B, w.N, w.H
+    assert np.array_equal(_bits(qz.k_mean.cpu().numpy()), _bits(ref.k_mean))
+    assert np.array_equal(_bits(qz.q_scale.cpu().numpy()), _bits(ref.q_scale))
+    assert np.array_equal(_bits(qz.k_scale.cpu().numpy()), _bits(ref.k_scale))
+    assert np.array_equal(_bits(qz.v_scale.cpu().numpy()), _bits(ref.v_scale))
+    assert np.array_equal(layouts.q_logical(qz.q_i8.cpu().numpy(), B, H, N), ref.q_i8)
+    assert np.array_equal(layouts.k_logical(qz.k_i8.cpu().numpy(), B, H, N), ref.k_i8)
+    assert np.array_equal(layouts.v_logical(qz.v_fp8.cpu().numpy(), B, H, N), ref.v8)
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    got_bits = two.view(torch.int16).cpu().numpy().view(np.uint16)
+    got = _dec_bf16(got_bits).astype(np.float64)
+    want = _dec_bf16(ref_bits).astype(np.float64)
+    assert np.max(np.abs(got - want)) <= MAX_ABS
+    assert _cos(got, want) >= MIN_COS
+    assert np.mean(got_bits == ref_bits) >= MIN_BIT_EQUAL
+
+
 def test_closed_form_v_ones_and_q_zero_on_gpu(sage):
     inp = _cpu_inputs("tiny")
     ones = torch.ones_like(inp.v).cuda()
